@@ -1,0 +1,154 @@
+"""Plain per-token definition of one step's compile, K/V write and gather.
+
+Test infrastructure only (see the package docstring).  Pure Python loops, one
+token at a time, written so each line can be checked against the pages:
+
+* query_start_loc is the running total of the per-request scheduled counts
+  ([P1 §第一步：从每请求 token 数得到边界]; [P3 §布局与元数据]).
+* token j of request i sits at model position c_i + j
+  ([P1 §第二步：相对位置加已计算长度得到模型位置]).
+* its input id is entry c_i + j of row i of the token table
+  ([P1 §第三步：从二维 token 历史抽取本轮切片]).
+* its K/V slot is block_table[i][p // B] * B + p % B
+  ([P1 §Block table 是逐请求的页表], worked out in [P1 §3. 物理 KV 槽位]).
+* seq_lens_i = c_i + q_i; logits index = last flat token of the request
+  ([P1 §第四步：只在必要位置计算 logits]; [P2 §8.6.3]).
+* a chunk that has not reached the end of the prompt is discarded
+  ([P1 §Chunked Prefill：query 很长，但仍只是一段区间]); the compacted list
+  keeps only requests that may sample ([P3 §练习 1. 元数据推导]).
+* padding to a captured size: pseudo-requests get empty intervals and padded
+  tokens go to the reserved null block ([P1 §固定地址与动态有效长度如何共存];
+  [P4 §5. 关键细节与坑]).
+* the t-th new K/V row is written to slot_mapping[t] with no request id
+  involved ([P1 §3. 物理 KV 槽位]; [P3 §实现]).
+
+Readings where the pages leave a value open (also listed in the design doc):
+
+* pad token t in [N, N_pad): input_id 0, position 0, req_index -1,
+  slot null_block * B.
+* pseudo-request i in [R, max_num_reqs): query_start_loc[i+1] = N,
+  seq_len 0, logits index -1, discard 1, sample index -1.
+* discard_i = (c_i + q_i < P_i), with P_i the prompt length.
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Sequence
+
+
+class StepError(ValueError):
+    """A precondition of the step does not hold."""
+
+
+def padded_size(capture_sizes: Sequence[int], num_tokens: int) -> int:
+    """Smallest captured size >= num_tokens; num_tokens itself above the
+    largest one (the step then runs unpadded).
+    [P2 §8.5.0.5 pad_for_cudagraph 的实现]; [P4 §3. 原理演示：向上取整的图派发]."""
+    for s in sorted(capture_sizes):
+        if s >= num_tokens:
+            return s
+    return num_tokens
+
+
+def compile_step(rows, *, block_size: int, max_num_reqs: int, max_model_len: int,
+                 max_num_batched_tokens: int, num_kv_blocks: int, n_pad: int,
+                 null_block: int = 0, check_unique_slots: bool = True) -> Dict:
+    """Compile the condensed rows 0..R-1 into the flat token stream.
+
+    ``rows[i]`` has ``num_computed`` (c), ``num_scheduled`` (q), ``num_prompt``
+    (P), ``tokens`` (the history, length T) and ``blocks`` (physical ids).
+    Returns a dict of lists; per-request lists have ``max_num_reqs`` entries
+    (query_start_loc has one more), per-token lists ``n_pad``.
+    """
+    R = len(rows)
+    B = block_size
+    if R > max_num_reqs:
+        raise StepError("more requests than rows")
+    for i, r in enumerate(rows):
+        c, q, T = r.num_computed, r.num_scheduled, len(r.tokens)
+        if q < 1:
+            raise StepError(f"request {i}: nothing scheduled")
+        if c < 0 or c + q > T:
+            raise StepError(f"request {i}: scheduled range outside the token history")
+        if T > max_model_len:
+            raise StepError(f"request {i}: history longer than max_model_len")
+        last_block = (c + q - 1) // B
+        if last_block >= len(r.blocks):
+            raise StepError(f"request {i}: too few blocks for position {c + q - 1}")
+        for b in r.blocks[:last_block + 1]:
+            if not (0 <= b < num_kv_blocks) or b == null_block:
+                raise StepError(f"request {i}: block id {b} not a usable block")
+
+    # query_start_loc: running total of the scheduled counts.
+    qsl = [0]
+    for r in rows:
+        qsl.append(qsl[-1] + r.num_scheduled)
+    N = qsl[R]
+    if N > n_pad:
+        raise StepError("padded size below the real token count")
+    if n_pad > max_num_batched_tokens:
+        raise StepError("padded size above the token budget")
+    for _ in range(R, max_num_reqs):
+        qsl.append(N)
+
+    input_ids: List[int] = []
+    positions: List[int] = []
+    req_indices: List[int] = []
+    slot_mapping: List[int] = []
+    for i, r in enumerate(rows):
+        for j in range(r.num_scheduled):
+            p = r.num_computed + j
+            req_indices.append(i)
+            positions.append(p)
+            input_ids.append(int(r.tokens[p]))
+            logical_block, offset = p // B, p % B
+            slot_mapping.append(int(r.blocks[logical_block]) * B + offset)
+    for _ in range(N, n_pad):
+        input_ids.append(0)
+        positions.append(0)
+        req_indices.append(-1)
+        slot_mapping.append(null_block * B)
+
+    if check_unique_slots and len(set(slot_mapping[:N])) != N:
+        raise StepError("two real tokens map to the same K/V slot")
+
+    seq_lens, logits_indices, discard = [], [], []
+    for i, r in enumerate(rows):
+        seq_lens.append(r.num_computed + r.num_scheduled)
+        logits_indices.append(qsl[i + 1] - 1)
+        discard.append(1 if r.num_computed + r.num_scheduled < r.num_prompt else 0)
+    sample_indices = [logits_indices[i] for i in range(R) if not discard[i]]
+    num_sampled = len(sample_indices)
+    for _ in range(R, max_num_reqs):
+        seq_lens.append(0)
+        logits_indices.append(-1)
+        discard.append(1)
+    sample_indices += [-1] * (max_num_reqs - num_sampled)
+
+    return dict(
+        query_start_loc=qsl, seq_lens=seq_lens, logits_indices=logits_indices,
+        discard=discard, sample_indices=sample_indices, num_sampled=num_sampled,
+        input_ids=input_ids, positions=positions, req_indices=req_indices,
+        slot_mapping=slot_mapping, num_reqs=R, num_actual_tokens=N, num_tokens_padded=n_pad,
+        max_query_len=max((r.num_scheduled for r in rows), default=0),
+        max_seq_len=max((r.num_computed + r.num_scheduled for r in rows), default=0),
+    )
+
+
+def reshape_and_cache(k_rows, v_rows, k_cache, v_cache, slot_mapping) -> None:
+    """Copy K row t and V row t into cache row slot_mapping[t], one token at a
+    time.  Rows are opaque byte strings (indexable objects whose items can be
+    assigned).  [P1 §3. 物理 KV 槽位]; [P3 §实现] (kv.write before attention)."""
+    for t, s in enumerate(slot_mapping):
+        k_cache[s] = k_rows[t]
+        v_cache[s] = v_rows[t]
+
+
+def gather_rows(src_rows, indices, count: int, zero_row):
+    """out[m] = src[indices[m]] for m < count; a negative index yields the zero
+    row.  [P2 §8.7 execute_model：完整主流程] (hidden_states[logits_indices]);
+    [P4 §4.1]."""
+    out = []
+    for m in range(count):
+        idx = indices[m]
+        out.append(zero_row if idx < 0 else src_rows[idx])
+    return out
