@@ -1,0 +1,275 @@
+/*
+ * ric.h - ragged input compilation for one step of a continuous-batching LLM
+ * runner, on AMD Instinct MI355X (gfx950).
+ *
+ * One step: a persistent, row-compacted request batch (a device-resident column
+ * store) is compiled into a flat 1-D token stream plus its attention metadata;
+ * the step's new K/V rows are then written into a paged cache through the slot
+ * mapping, and hidden states are gathered at the rows that produce logits.
+ *
+ * Sources, cited by page title and section:
+ *   [P1] "vLLM 源码完全拆解（五）：GPUModelRunner 如何把动态请求拼成一次 GPU 前向"
+ *   [P2] "第8章 ModelRunner：从 SchedulerOutput 到 GPU Kernel"
+ *   [P3] "变长批处理与一次混合前向"
+ *   [P4] "04 · 模型执行与 CUDA Graph"
+ *   [P5] "Nano-VLLM全代码解析笔记(4)-model_runner"
+ *
+ * Conventions for every call:
+ *   - Return value: RIC_OK (0) or a negative RIC_E* code.  On error nothing
+ *     has changed (no host state, no device work enqueued) and
+ *     ric_last_error() holds a message for the calling thread.
+ *   - "device" pointers are HIP device addresses (e.g. torch tensor
+ *     data_ptr()); "host" pointers are ordinary host memory.  Host input arrays
+ *     are read (and copied into pinned staging where needed) before the call
+ *     returns, so the caller may reuse them at once.
+ *   - Device work is enqueued on a HIP stream and is asynchronous.  No call on
+ *     the step path (schedule, compile, reshape_and_cache, gather) waits for
+ *     the device or copies device data to the host.
+ *   - Integer values are int32; byte offsets are computed in 64 bits.
+ */
+#ifndef RIC_H
+#define RIC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RIC_OK      0
+#define RIC_EINVAL (-1)  /* an argument or a step precondition is invalid      */
+#define RIC_ENOMEM (-2)  /* device or pinned host allocation failed            */
+#define RIC_EFULL  (-3)  /* no free row, or a row's token / block capacity     */
+#define RIC_ENOENT (-4)  /* unknown request id                                 */
+#define RIC_EEXIST (-5)  /* request id already live                            */
+#define RIC_ERANGE (-6)  /* a value is outside the configured capacity         */
+#define RIC_EHIP   (-7)  /* a HIP runtime call failed                          */
+#define RIC_ESTATE (-8)  /* call order: e.g. compile without a fresh schedule  */
+
+typedef struct ric_batch ric_batch;   /* opaque handle: column store + step buffers */
+
+/* Capacities, fixed at creation. */
+typedef struct {
+    int32_t max_num_reqs;            /* rows of the persistent batch (<= 8000)            */
+    int32_t max_model_len;           /* token-history capacity per row                    */
+    int32_t block_size;              /* tokens per K/V block, B >= 1                      */
+    int32_t max_blocks_per_req;      /* block-table capacity per row                      */
+    int32_t max_num_batched_tokens;  /* capacity of the per-token outputs (padded count)  */
+    int32_t num_kv_blocks;           /* physical blocks in the cache; num_kv_blocks*B < 2^31 */
+    int32_t null_block;              /* reserved block for padded tokens (usually 0)      */
+    int32_t staging_bytes;           /* pinned delta-staging capacity; 0 = default (4 MiB) */
+} ric_config;
+
+/* Per-request sampling values.  They live in the column store and move with
+ * their row; sampling itself is not part of this library.  [P2 §8.2.1]. */
+typedef struct {
+    float temperature;
+    float top_p;
+    float repetition_penalty;
+    int32_t top_k;
+} ric_sampling;
+
+/* Outputs of ric_compile.  The device pointers are owned by the handle, keep
+ * the same address for the handle's lifetime and are rewritten by every
+ * compile (fixed-address buffers with a valid prefix, [P1 §固定地址与动态有效长度如何共存]).
+ * Per-token arrays hold max_num_batched_tokens entries, of which the first
+ * num_tokens_padded are written; per-request arrays hold max_num_reqs entries
+ * (query_start_loc one more), all written. */
+typedef struct {
+    int32_t* input_ids;        /* [t] token id at position positions[t] of request req_indices[t]; pad: 0 */
+    int32_t* positions;        /* [t] c_r + (t - qsl[r]); pad: 0                                */
+    int32_t* req_indices;      /* [t] row r owning token t; pad: -1                              */
+    int32_t* slot_mapping;     /* [t] block_table[r][p/B]*B + p%B; pad: null_block*B             */
+    int32_t* query_start_loc;  /* [i] exclusive prefix sum of q; entries past R hold N           */
+    int32_t* seq_lens;         /* [i] c_i + q_i; 0 past R                                        */
+    int32_t* logits_indices;   /* [i] qsl[i+1]-1; -1 past R                                      */
+    uint8_t* discard;          /* [i] 1 if c_i + q_i < prompt_i (partial prefill); 1 past R      */
+    int32_t* sample_indices;   /* logits_indices of the rows with discard == 0, in row order; -1 after */
+    int32_t* dev_scalars;      /* [8] device: R, N, N_pad, max_query_len, max_seq_len, num_sampled,
+                                  [6] tokens whose column data was out of range since creation
+                                  (always 0 unless device memory was corrupted), [7] unused */
+    /* host values of this step (from the host mirror of the counters) */
+    int32_t num_reqs;          /* R */
+    int32_t num_actual_tokens; /* N = sum of q */
+    int32_t num_tokens_padded; /* N_pad */
+    int32_t max_query_len;
+    int32_t max_seq_len;
+    int32_t num_sampled;
+} ric_step;
+
+/* Device views of the column store (for inspection and tests).  Row r of the
+ * token table starts at tokens + r*token_stride; of the block table at
+ * blocks + r*block_stride.  Scalar columns hold max_num_reqs entries each. */
+typedef struct {
+    int32_t* tokens;           /* [max_num_reqs][token_stride] int32 */
+    int32_t* blocks;           /* [max_num_reqs][block_stride] int32 */
+    int64_t token_stride;
+    int64_t block_stride;
+    int32_t* num_tokens;       /* T_r: valid history length       */
+    int32_t* num_prompt;       /* P_r                              */
+    int32_t* num_computed;     /* c_r (from the last schedule)     */
+    int32_t* num_scheduled;    /* q_r (from the last schedule)     */
+    int32_t* num_blocks;       /* valid block-table entries        */
+    int32_t* top_k;
+    float* temperature;
+    float* top_p;
+    float* repetition_penalty;
+} ric_columns;
+
+/* ---- handle -------------------------------------------------------------- */
+
+/* Device bytes a handle needs for `cfg` (column store + step outputs + staging). */
+size_t ric_workspace_bytes(const ric_config* cfg);
+
+/* Create a handle.  `stream` (hipStream_t, may be NULL for the default stream)
+ * orders all of the handle's device work.  `workspace` is a device buffer of at
+ * least ric_workspace_bytes(cfg) bytes owned by the caller (e.g. a torch
+ * tensor), or NULL for the library to allocate its own.  The pinned host
+ * staging is always allocated by the library.  Errors: EINVAL (capacities),
+ * ENOMEM, EHIP. */
+int ric_create(const ric_config* cfg, void* stream, void* workspace, size_t workspace_bytes,
+               ric_batch** out);
+
+/* Wait for the handle's stream, free what the library allocated.  A NULL
+ * handle is accepted. */
+int ric_destroy(ric_batch* b);
+
+/* Change the stream later calls enqueue on (ordering with earlier work is the
+ * caller's business). */
+int ric_set_stream(ric_batch* b, void* stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* ric_last_error(void);
+
+/* ---- column-store deltas ([P1 §新请求建立完整状态], [P1 §驻留请求只合并差量],
+ *      [P2 §8.2.2 三种变更操作]).  Each call updates the host mirror at once and
+ *      stages its payload; staged payloads reach the device column store in one
+ *      upload plus one scatter kernel at the next flush (explicit ric_flush,
+ *      ric_condense or ric_compile, or when staging fills). */
+
+/* Install a new request in the lowest free row: token history tokens[0,T),
+ * prompt length, computed count, block ids blocks[0,nb) (each in
+ * [0, num_kv_blocks) and not the null block), sampling values (NULL: 1,1,1,0).
+ * A request aborted and resubmitted under the same id must be removed first
+ * ([P2 §8.2.2.6]).  Errors: EEXIST, EFULL (no free row), ERANGE (T >
+ * max_model_len, nb > max_blocks_per_req, counts outside [0,T], bad block id). */
+int ric_add_request(ric_batch* b, uint64_t req_id, const int32_t* tokens, int32_t num_tokens,
+                    int32_t num_prompt, int32_t num_computed, const int32_t* blocks,
+                    int32_t num_blocks, const ric_sampling* sampling, int32_t* out_row);
+
+/* Remove a request (finished, or unscheduled/preempted): its row becomes a
+ * hole until ric_condense or a later add fills it.  Errors: ENOENT. */
+int ric_remove_request(ric_batch* b, uint64_t req_id, int32_t* out_row);
+
+/* Append new token ids to the request's history.  Errors: ENOENT, EFULL. */
+int ric_append_tokens(ric_batch* b, uint64_t req_id, const int32_t* ids, int32_t n);
+
+/* Append newly allocated block ids to the request's block-table row.
+ * Errors: ENOENT, EFULL, ERANGE (bad block id). */
+int ric_append_blocks(ric_batch* b, uint64_t req_id, const int32_t* ids, int32_t n);
+
+/* Replace the whole block-table row (a request resumed after preemption: its
+ * old ids are no longer valid, [P1 §驻留请求只合并差量]).  Errors as append. */
+int ric_replace_blocks(ric_batch* b, uint64_t req_id, const int32_t* ids, int32_t n);
+
+/* Fill holes so the live rows are exactly [0, R): the k-th lowest hole
+ * receives the k-th highest live row while the hole lies below it, and every
+ * column of a moved row moves with it (token history, block row, counters,
+ * sampling values) in one kernel ([P1 §行号是一种短生命周期地址],
+ * [P1 §为什么删除后还要压紧]).  *out_num_moved = rows moved.  Flushes staged
+ * deltas first. */
+int ric_condense(ric_batch* b, int32_t* out_num_moved);
+
+/* Upload staged deltas now. */
+int ric_flush(ric_batch* b);
+
+/* Number of live requests; row of a request (or RIC_ENOENT); request at a row
+ * (RIC_ENOENT for a hole). */
+int32_t ric_num_reqs(const ric_batch* b);
+int32_t ric_row_of(const ric_batch* b, uint64_t req_id);
+int ric_req_at(const ric_batch* b, int32_t row, uint64_t* out_req_id);
+
+/* Device views of the columns. */
+int ric_get_columns(const ric_batch* b, ric_columns* out);
+
+/* Wait until the handle's stream is idle (tests, teardown; not a step call). */
+int ric_sync(ric_batch* b);
+
+/* ---- step ---------------------------------------------------------------- */
+
+/* This step's counts for rows 0..R-1 (host arrays of R entries): cached
+ * length c_i and scheduled count q_i ([P1 §第一步], [P1 §第二步]).  Checked
+ * in O(R) against the host mirror: live rows are exactly [0,R) (condensed),
+ * q_i >= 1, c_i >= 0, c_i + q_i <= T_i, ceil((c_i+q_i)/B) <= blocks of row i,
+ * sum q_i <= max_num_batched_tokens.  Errors: EINVAL, ESTATE (holes). */
+int ric_schedule(ric_batch* b, int32_t num_reqs, const int32_t* num_computed,
+                 const int32_t* num_scheduled);
+
+/* Compile the scheduled batch into the flat token stream and its metadata in
+ * one kernel: query_start_loc, req_indices, positions, input_ids, slot_mapping,
+ * seq_lens, logits_indices, discard, sample_indices and the device scalars
+ * ([P1 §第一步..第四步], [P1 §Block table 是逐请求的页表], [P3 §布局与元数据]).
+ * Tokens [N, num_tokens_padded) are padding: they map to the null block
+ * ([P1 §固定地址与动态有效长度如何共存], [P4 §5]).  Requires a ric_schedule
+ * since the last row-changing call.  Errors: ESTATE, EINVAL (N > N_pad or
+ * N_pad > max_num_batched_tokens). */
+int ric_compile(ric_batch* b, int32_t num_tokens_padded, ric_step* out);
+
+/* Write the step's new K/V rows into paged caches through a slot mapping
+ * ([P1 §3. 物理 KV 槽位], [P3 §实现]: the t-th row goes to slot_mapping[t]).
+ *   k[l], v[l]        host arrays of num_layers DEVICE pointers: source row t
+ *                     starts at k[l] + t*src_row_stride (bytes; 0 = row_bytes)
+ *   k_cache[l], v_cache[l]  host arrays of DEVICE pointers: cache row s starts
+ *                     at k_cache[l] + s*row_bytes; s < num_slots
+ *                     (layout [num_blocks, B, kv_heads, head_dim])
+ *   slot_mapping      DEVICE int32[num_tokens]
+ *   row_bytes         bytes of one token's K (or V) row; multiple of 16;
+ *                     src_row_stride and every pointer 16-byte aligned
+ *   dev_status        optional DEVICE int32: incremented once per row whose
+ *                     slot is outside [0, num_slots) (that row is not written)
+ * All layers are written by one launch.  Errors: EINVAL (alignment, counts),
+ * EHIP. */
+int ric_reshape_and_cache(const void* const* k, const void* const* v, void* const* k_cache,
+                          void* const* v_cache, int32_t num_layers, const int32_t* slot_mapping,
+                          int32_t num_tokens, int64_t src_row_stride, int32_t row_bytes,
+                          int64_t num_slots, int32_t* dev_status, void* stream);
+
+/* Gather rows: dst[m] = src[idx[m]] for m < count, where count = *dev_count
+ * (DEVICE int32, e.g. ric_step.dev_scalars + 5 for the compacted list) or
+ * max_rows when dev_count is NULL.  A negative index yields a zero row; an
+ * index >= src_rows yields a zero row and bumps *dev_status if given.  Rows
+ * m in [count, max_rows) of dst are left untouched.  Used for hidden states at
+ * logits_indices / sample_indices ([P2 §8.7], [P4 §4.1]).  Pointers and
+ * strides 16-byte aligned, row_bytes a multiple of 16.  Errors: EINVAL, EHIP. */
+int ric_gather_rows(const void* src, int64_t src_row_stride, int64_t src_rows,
+                    const int32_t* idx, const int32_t* dev_count, int32_t max_rows,
+                    int32_t row_bytes, void* dst, int64_t dst_row_stride, int32_t* dev_status,
+                    void* stream);
+
+/* ---- host-only helpers (no device work) ----------------------------------- */
+
+/* Smallest of the n capture sizes >= num_tokens; num_tokens itself when it
+ * exceeds them all ([P2 §8.5.0.5], [P4 §3]).  Sizes need not be sorted.
+ * Returns RIC_EINVAL for num_tokens < 0 or n < 0. */
+int32_t ric_padded_size(const int32_t* capture_sizes, int32_t n, int32_t num_tokens);
+
+/* Condense plan for a row-occupancy mask live[0..num_rows): writes the
+ * (hole, source) pairs the handle would use and returns their count. */
+int32_t ric_condense_plan(const uint8_t* live, int32_t num_rows, int32_t* holes,
+                          int32_t* sources);
+
+/* Check a step against the rules of ric_schedule/ric_compile from host
+ * counters of rows 0..R-1 (c, q, prompt P, history T, blocks nb) and fill the
+ * host scalars of *out (device pointers left NULL).  Returns RIC_OK or the
+ * error the handle would return. */
+int ric_check_step(const ric_config* cfg, int32_t num_reqs, const int32_t* num_computed,
+                   const int32_t* num_scheduled, const int32_t* num_prompt,
+                   const int32_t* num_tokens, const int32_t* num_blocks,
+                   int32_t num_tokens_padded, ric_step* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RIC_H */

@@ -1,0 +1,20 @@
+"""ric: ragged input compilation for MI355X (gfx950).
+
+The product is the C-ABI library ``libric.so`` (declared in ``include/ric.h``),
+built in-tree by ``python -m ragged_input_compilation_amd.build``.  The Python
+side is a thin ctypes binding (``_ric``) plus a step driver (``runner``) that
+allocates device memory and streams with PyTorch and calls the library.
+Importing ``_ric`` fails loudly when the library has not been built: there is no
+fallback implementation."""
+
+__all__ = ["ric", "runner"]
+
+
+def __getattr__(name):
+    if name == "ric":
+        from . import _ric
+        return _ric
+    if name == "runner":
+        from . import runner
+        return runner
+    raise AttributeError(name)

@@ -1,0 +1,836 @@
+// Host control plane and C ABI of libric: the persistent batch's row maps and
+// counters (host mirror), validation, delta staging, and the launches.
+//
+// Sources (page title, section):
+//   [P1] "vLLM 源码完全拆解（五）：GPUModelRunner 如何把动态请求拼成一次 GPU 前向"
+//   [P2] "第8章 ModelRunner：从 SchedulerOutput 到 GPU Kernel"
+//   [P4] "04 · 模型执行与 CUDA Graph"
+//
+// The device holds the column store; the host keeps only what validation and
+// row bookkeeping need (row <-> request maps and the per-row scalar columns).
+// Token and block payloads never live on the host beyond the pinned staging:
+// each mutation appends its payload to a pinned log, and a flush uploads the
+// whole log with one copy and scatters it with one kernel, instead of one
+// small copy per request.  Two pinned logs alternate, each guarded by an event
+// so the host never overwrites a log that a copy may still be reading
+// ([P1 §为什么 CPU 侧同时要 tensor 和 NumPy view]: producer/consumer ordering
+// of pinned buffers).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "../../include/ric.h"
+#include "ric_internal.h"
+
+using namespace ric;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+#define HIP_TRY(expr)                                                                   \
+    do {                                                                                \
+        hipError_t e_ = (expr);                                                         \
+        if (e_ != hipSuccess) return fail(RIC_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+    } while (0)
+
+constexpr size_t kAlign = 256;
+constexpr uint32_t kMaxWordsPerOp = 8192;   // split big payloads so ops spread over workgroups
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int64_t round4(int64_t x) { return (x + 3) / 4 * 4; }
+
+int ilog2_exact(int64_t x) {
+    if (x <= 0 || (x & (x - 1)) != 0) return -1;
+    int s = 0;
+    while ((int64_t(1) << s) < x) ++s;
+    return s;
+}
+
+struct Layout {
+    int64_t tok_stride, blk_stride;
+    size_t off_tok, off_blk, off_scal, off_ids, off_pos, off_req, off_slot, off_qsl, off_seq,
+        off_logits, off_sample, off_discard, off_dscal, off_pairs, off_staging, total;
+    size_t staging_bytes;
+};
+
+size_t default_staging(const ric_config& c) {
+    const size_t scal_reserve = (size_t)kNumScalarCols * (size_t)c.max_num_reqs * 4 + 64 * 16;
+    return std::max<size_t>(4u << 20, 4 * scal_reserve);
+}
+
+Layout layout_of(const ric_config& c) {
+    Layout L{};
+    L.tok_stride = round4(c.max_model_len);
+    L.blk_stride = round4(c.max_blocks_per_req);
+    L.staging_bytes = c.staging_bytes > 0 ? (size_t)c.staging_bytes : default_staging(c);
+    const size_t R = (size_t)c.max_num_reqs, NT = (size_t)c.max_num_batched_tokens;
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = o;
+        o = align_up(o + bytes, kAlign);
+        return at;
+    };
+    L.off_tok = take(R * (size_t)L.tok_stride * 4);
+    L.off_blk = take(R * (size_t)L.blk_stride * 4);
+    L.off_scal = take((size_t)kNumScalarCols * R * 4);
+    L.off_ids = take(NT * 4);
+    L.off_pos = take(NT * 4);
+    L.off_req = take(NT * 4);
+    L.off_slot = take(NT * 4);
+    L.off_qsl = take((R + 1) * 4);
+    L.off_seq = take(R * 4);
+    L.off_logits = take(R * 4);
+    L.off_sample = take(R * 4);
+    L.off_discard = take(R);
+    L.off_dscal = take(kNumDevScalars * 4);
+    L.off_pairs = take(R * 2 * 4);
+    L.off_staging = take(L.staging_bytes);
+    L.total = o;
+    return L;
+}
+
+int check_config(const ric_config* c) {
+    if (!c) return fail(RIC_EINVAL, "config is NULL");
+    if (c->max_num_reqs < 1 || c->max_num_reqs > kMaxReqsLimit)
+        return fail(RIC_EINVAL, "max_num_reqs must be in [1, %d]", kMaxReqsLimit);
+    if (c->max_model_len < 1 || c->block_size < 1 || c->max_blocks_per_req < 1 ||
+        c->max_num_batched_tokens < 1 || c->num_kv_blocks < 1)
+        return fail(RIC_EINVAL, "capacities must be positive");
+    if (c->null_block < 0 || c->null_block >= c->num_kv_blocks)
+        return fail(RIC_EINVAL, "null_block outside [0, num_kv_blocks)");
+    if ((int64_t)c->num_kv_blocks * c->block_size >= (int64_t(1) << 31))
+        return fail(RIC_EINVAL, "num_kv_blocks * block_size must stay below 2^31 (int32 slots)");
+    if (c->staging_bytes < 0) return fail(RIC_EINVAL, "staging_bytes negative");
+    if (c->staging_bytes > 0 && (size_t)c->staging_bytes < default_staging(*c) / 4 + 4096)
+        return fail(RIC_EINVAL, "staging_bytes too small for the scalar columns");
+    return RIC_OK;
+}
+
+}  // namespace
+
+struct ric_batch {
+    ric_config cfg{};
+    Layout L{};
+    hipStream_t stream = nullptr;
+    int device = 0;
+    bool own_ws = false;
+    uint8_t* ws = nullptr;
+
+    // device regions
+    int32_t *d_tok = nullptr, *d_blk = nullptr, *d_scal = nullptr;
+    int32_t *d_ids = nullptr, *d_pos = nullptr, *d_req = nullptr, *d_slot = nullptr;
+    int32_t *d_qsl = nullptr, *d_seq = nullptr, *d_logits = nullptr, *d_sample = nullptr;
+    uint8_t* d_discard = nullptr;
+    int32_t *d_dscal = nullptr, *d_pairs = nullptr;
+    uint8_t* d_staging = nullptr;
+
+    // pinned delta logs
+    uint8_t* h_log[2] = {nullptr, nullptr};
+    hipEvent_t ev[2] = {nullptr, nullptr};
+    bool ev_pending[2] = {false, false};
+    int cur = 0;
+    bool cur_ready = false;          // h_log[cur] is known free to write
+    uint32_t payload_words = 0;
+    std::vector<DeltaOp> ops;
+    uint32_t epoch = 1;
+
+    // host mirror
+    std::vector<int32_t> scal;       // [kNumScalarCols][max_num_reqs]
+    int32_t dirty_lo[kNumScalarCols], dirty_hi[kNumScalarCols];
+    std::vector<uint64_t> req_at;
+    std::vector<uint8_t> live;
+    std::vector<uint32_t> pending_epoch;
+    std::unordered_map<uint64_t, int32_t> row_of;
+    int32_t num_live = 0;
+
+    // schedule state
+    bool scheduled = false;
+    int32_t sched_R = 0, sched_N = 0, sched_max_q = 0, sched_max_seq = 0, sched_sampled = 0;
+
+    int32_t& S(int col, int row) { return scal[(size_t)col * cfg.max_num_reqs + row]; }
+    int32_t* dcol(int col) { return d_scal + (size_t)col * cfg.max_num_reqs; }
+
+    void mark(int col, int row) {
+        dirty_lo[col] = std::min(dirty_lo[col], row);
+        dirty_hi[col] = std::max(dirty_hi[col], row + 1);
+    }
+    void clear_dirty() {
+        for (int c = 0; c < kNumScalarCols; ++c) {
+            dirty_lo[c] = cfg.max_num_reqs;
+            dirty_hi[c] = 0;
+        }
+    }
+    int32_t used_rows() const {
+        for (int32_t r = cfg.max_num_reqs - 1; r >= 0; --r)
+            if (live[r]) return r + 1;
+        return 0;
+    }
+};
+
+namespace {
+
+// Bytes the log needs for everything staged so far plus `extra_words` more
+// payload in one more op, plus the scalar columns a flush appends.
+size_t log_need(const ric_batch* b, size_t extra_words, size_t extra_ops) {
+    const size_t scal_words = (size_t)kNumScalarCols * b->cfg.max_num_reqs;
+    return align_up(((size_t)b->payload_words + extra_words + scal_words) * 4, 16) +
+           (b->ops.size() + extra_ops + kNumScalarCols) * sizeof(DeltaOp);
+}
+
+int ensure_log_writable(ric_batch* b) {
+    if (b->cur_ready) return RIC_OK;
+    if (b->ev_pending[b->cur]) {
+        HIP_TRY(hipEventSynchronize(b->ev[b->cur]));
+        b->ev_pending[b->cur] = false;
+    }
+    b->cur_ready = true;
+    return RIC_OK;
+}
+
+uint32_t* log_payload(ric_batch* b) { return reinterpret_cast<uint32_t*>(b->h_log[b->cur]); }
+
+int flush(ric_batch* b);
+
+// Stage `n` words for device address `dst`, splitting across ops and flushes.
+int stage(ric_batch* b, void* dst, const void* src, size_t n) {
+    const uint8_t* s = static_cast<const uint8_t*>(src);
+    uint8_t* d = static_cast<uint8_t*>(dst);
+    while (n > 0) {
+        size_t take = std::min<size_t>(n, kMaxWordsPerOp);
+        if (log_need(b, take, 1) > b->L.staging_bytes) {
+            // shrink to what fits, or flush if nothing does
+            size_t lo = 0, hi = take;
+            while (lo < hi) {
+                const size_t mid = (lo + hi + 1) / 2;
+                if (log_need(b, mid, 1) <= b->L.staging_bytes) lo = mid; else hi = mid - 1;
+            }
+            take = lo;
+            if (take == 0) {
+                int rc = flush(b);
+                if (rc) return rc;
+                continue;
+            }
+        }
+        int rc = ensure_log_writable(b);
+        if (rc) return rc;
+        memcpy(log_payload(b) + b->payload_words, s, take * 4);
+        b->ops.push_back(DeltaOp{reinterpret_cast<uint64_t>(d), b->payload_words, (uint32_t)take});
+        b->payload_words += (uint32_t)take;
+        s += take * 4;
+        d += take * 4;
+        n -= take;
+    }
+    return RIC_OK;
+}
+
+int flush(ric_batch* b) {
+    bool any_dirty = false;
+    for (int c = 0; c < kNumScalarCols; ++c) any_dirty |= b->dirty_lo[c] < b->dirty_hi[c];
+    if (b->ops.empty() && !any_dirty) return RIC_OK;
+    int rc = ensure_log_writable(b);
+    if (rc) return rc;
+    // Scalar columns: copy the dirty row range of each column from the mirror.
+    // (Room for them is always reserved by log_need.)
+    for (int c = 0; c < kNumScalarCols; ++c) {
+        if (b->dirty_lo[c] >= b->dirty_hi[c]) continue;
+        const int32_t lo = b->dirty_lo[c], n = b->dirty_hi[c] - lo;
+        memcpy(log_payload(b) + b->payload_words, &b->S(c, lo), (size_t)n * 4);
+        b->ops.push_back(DeltaOp{reinterpret_cast<uint64_t>(b->dcol(c) + lo), b->payload_words, (uint32_t)n});
+        b->payload_words += (uint32_t)n;
+    }
+    const size_t ops_off = align_up((size_t)b->payload_words * 4, 16);
+    const size_t ops_bytes = b->ops.size() * sizeof(DeltaOp);
+    if (ops_off + ops_bytes > b->L.staging_bytes) return fail(RIC_EHIP, "internal: delta log overflow");
+    memcpy(b->h_log[b->cur] + ops_off, b->ops.data(), ops_bytes);
+    HIP_TRY(hipMemcpyAsync(b->d_staging, b->h_log[b->cur], ops_off + ops_bytes, hipMemcpyHostToDevice,
+                           b->stream));
+    HIP_TRY(launch_apply_deltas(reinterpret_cast<const uint32_t*>(b->d_staging),
+                                reinterpret_cast<const DeltaOp*>(b->d_staging + ops_off),
+                                (int)b->ops.size(), b->stream));
+    HIP_TRY(hipEventRecord(b->ev[b->cur], b->stream));
+    b->ev_pending[b->cur] = true;
+    b->cur ^= 1;
+    b->cur_ready = false;
+    b->payload_words = 0;
+    b->ops.clear();
+    b->clear_dirty();
+    ++b->epoch;
+    return RIC_OK;
+}
+
+// Flush first when a new whole-row write could overlap a staged write to the
+// same row (ops of one flush are applied in parallel).
+int before_row_overwrite(ric_batch* b, int32_t row) {
+    if (b->pending_epoch[row] == b->epoch) return flush(b);
+    return RIC_OK;
+}
+
+int check_blocks(const ric_batch* b, const int32_t* ids, int32_t n) {
+    for (int32_t i = 0; i < n; ++i)
+        if (ids[i] < 0 || ids[i] >= b->cfg.num_kv_blocks || ids[i] == b->cfg.null_block)
+            return fail(RIC_ERANGE, "block id %d at index %d is not a usable block", ids[i], i);
+    return RIC_OK;
+}
+
+int find(const ric_batch* b, uint64_t req_id, int32_t* row) {
+    auto it = b->row_of.find(req_id);
+    if (it == b->row_of.end()) return fail(RIC_ENOENT, "unknown request id %llu", (unsigned long long)req_id);
+    *row = it->second;
+    return RIC_OK;
+}
+
+int32_t as_bits(float f) {
+    int32_t i;
+    memcpy(&i, &f, 4);
+    return i;
+}
+
+// Validation shared by ric_schedule and ric_check_step.
+int check_step_rows(const ric_config& cfg, int32_t R, const int32_t* c, const int32_t* q,
+                    const int32_t* P, const int32_t* T, const int32_t* nb, int32_t* N_out,
+                    int32_t* maxq_out, int32_t* maxseq_out, int32_t* sampled_out) {
+    if (R < 0 || R > cfg.max_num_reqs) return fail(RIC_EINVAL, "num_reqs %d outside [0, max_num_reqs]", R);
+    if (R > 0 && (!c || !q)) return fail(RIC_EINVAL, "count arrays are NULL");
+    int64_t N = 0;
+    int32_t maxq = 0, maxseq = 0, sampled = 0;
+    for (int32_t i = 0; i < R; ++i) {
+        if (q[i] < 1) return fail(RIC_EINVAL, "row %d: num_scheduled %d < 1", i, q[i]);
+        if (c[i] < 0) return fail(RIC_EINVAL, "row %d: num_computed %d < 0", i, c[i]);
+        const int64_t end = (int64_t)c[i] + q[i];
+        if (end > T[i]) return fail(RIC_EINVAL, "row %d: c+q = %lld exceeds the %d-token history", i, (long long)end, T[i]);
+        if ((end + cfg.block_size - 1) / cfg.block_size > nb[i])
+            return fail(RIC_EINVAL, "row %d: %d blocks cannot hold position %lld", i, nb[i], (long long)(end - 1));
+        N += q[i];
+        maxq = std::max(maxq, q[i]);
+        maxseq = std::max<int32_t>(maxseq, (int32_t)end);
+        sampled += (end >= P[i]) ? 1 : 0;
+    }
+    if (N > cfg.max_num_batched_tokens)
+        return fail(RIC_EINVAL, "%lld scheduled tokens exceed max_num_batched_tokens %d", (long long)N, cfg.max_num_batched_tokens);
+    *N_out = (int32_t)N;
+    *maxq_out = maxq;
+    *maxseq_out = maxseq;
+    *sampled_out = sampled;
+    return RIC_OK;
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+const char* ric_last_error(void) { return g_err.c_str(); }
+
+size_t ric_workspace_bytes(const ric_config* cfg) {
+    if (check_config(cfg)) return 0;
+    return layout_of(*cfg).total;
+}
+
+int ric_create(const ric_config* cfg, void* stream, void* workspace, size_t workspace_bytes, ric_batch** out) {
+    if (!out) return fail(RIC_EINVAL, "out is NULL");
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    ric_batch* b = new (std::nothrow) ric_batch();
+    if (!b) return fail(RIC_ENOMEM, "host allocation failed");
+    b->cfg = *cfg;
+    b->L = layout_of(*cfg);
+    b->stream = static_cast<hipStream_t>(stream);
+    auto bail = [&](int code) {
+        ric_destroy(b);
+        return code;
+    };
+    if (hipGetDevice(&b->device) != hipSuccess) return bail(fail(RIC_EHIP, "no HIP device"));
+    if (workspace) {
+        if (workspace_bytes < b->L.total)
+            return bail(fail(RIC_EINVAL, "workspace of %zu bytes, %zu needed", workspace_bytes, b->L.total));
+        if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+            return bail(fail(RIC_EINVAL, "workspace must be %zu-byte aligned", kAlign));
+        b->ws = static_cast<uint8_t*>(workspace);
+    } else {
+        if (hipMalloc(&b->ws, b->L.total) != hipSuccess) {
+            b->ws = nullptr;
+            return bail(fail(RIC_ENOMEM, "hipMalloc of %zu bytes failed", b->L.total));
+        }
+        b->own_ws = true;
+    }
+    const Layout& L = b->L;
+    b->d_tok = reinterpret_cast<int32_t*>(b->ws + L.off_tok);
+    b->d_blk = reinterpret_cast<int32_t*>(b->ws + L.off_blk);
+    b->d_scal = reinterpret_cast<int32_t*>(b->ws + L.off_scal);
+    b->d_ids = reinterpret_cast<int32_t*>(b->ws + L.off_ids);
+    b->d_pos = reinterpret_cast<int32_t*>(b->ws + L.off_pos);
+    b->d_req = reinterpret_cast<int32_t*>(b->ws + L.off_req);
+    b->d_slot = reinterpret_cast<int32_t*>(b->ws + L.off_slot);
+    b->d_qsl = reinterpret_cast<int32_t*>(b->ws + L.off_qsl);
+    b->d_seq = reinterpret_cast<int32_t*>(b->ws + L.off_seq);
+    b->d_logits = reinterpret_cast<int32_t*>(b->ws + L.off_logits);
+    b->d_sample = reinterpret_cast<int32_t*>(b->ws + L.off_sample);
+    b->d_discard = b->ws + L.off_discard;
+    b->d_dscal = reinterpret_cast<int32_t*>(b->ws + L.off_dscal);
+    b->d_pairs = reinterpret_cast<int32_t*>(b->ws + L.off_pairs);
+    b->d_staging = b->ws + L.off_staging;
+    for (int i = 0; i < 2; ++i) {
+        void* p = nullptr;
+        if (hipHostMalloc(&p, L.staging_bytes, hipHostMallocDefault) != hipSuccess)
+            return bail(fail(RIC_ENOMEM, "pinned staging allocation failed"));
+        b->h_log[i] = static_cast<uint8_t*>(p);
+        if (hipEventCreateWithFlags(&b->ev[i], hipEventDisableTiming) != hipSuccess)
+            return bail(fail(RIC_EHIP, "event creation failed"));
+    }
+    const int MR = cfg->max_num_reqs;
+    b->scal.assign((size_t)kNumScalarCols * MR, 0);
+    b->req_at.assign(MR, 0);
+    b->live.assign(MR, 0);
+    b->pending_epoch.assign(MR, 0);
+    b->clear_dirty();
+    // Scalar columns start at zero on the device too (the whole region).
+    for (int c = 0; c < kNumScalarCols; ++c) {
+        b->dirty_lo[c] = 0;
+        b->dirty_hi[c] = MR;
+    }
+    // Device scalars: [6] counts tokens whose row data was out of range (sticky).
+    const int32_t zeros[kNumDevScalars] = {0, 0, 0, 0, 0, 0, 0, 0};
+    rc = stage(b, b->d_dscal, zeros, kNumDevScalars);
+    if (rc) return bail(rc);
+    rc = flush(b);
+    if (rc) return bail(rc);
+    *out = b;
+    return RIC_OK;
+}
+
+int ric_destroy(ric_batch* b) {
+    if (!b) return RIC_OK;
+    if (b->ws) (void)hipStreamSynchronize(b->stream);
+    for (int i = 0; i < 2; ++i) {
+        if (b->ev[i]) (void)hipEventDestroy(b->ev[i]);
+        if (b->h_log[i]) (void)hipHostFree(b->h_log[i]);
+    }
+    if (b->own_ws && b->ws) (void)hipFree(b->ws);
+    delete b;
+    return RIC_OK;
+}
+
+int ric_set_stream(ric_batch* b, void* stream) {
+    if (!b) return fail(RIC_EINVAL, "handle is NULL");
+    HIP_TRY(hipStreamSynchronize(b->stream));
+    b->stream = static_cast<hipStream_t>(stream);
+    return RIC_OK;
+}
+
+int ric_add_request(ric_batch* b, uint64_t req_id, const int32_t* tokens, int32_t num_tokens,
+                    int32_t num_prompt, int32_t num_computed, const int32_t* blocks, int32_t num_blocks,
+                    const ric_sampling* sampling, int32_t* out_row) {
+    if (!b) return fail(RIC_EINVAL, "handle is NULL");
+    if (b->row_of.count(req_id)) return fail(RIC_EEXIST, "request id %llu is live", (unsigned long long)req_id);
+    if (num_tokens < 0 || num_tokens > b->cfg.max_model_len)
+        return fail(RIC_ERANGE, "num_tokens %d outside [0, max_model_len %d]", num_tokens, b->cfg.max_model_len);
+    if (num_blocks < 0 || num_blocks > b->cfg.max_blocks_per_req)
+        return fail(RIC_ERANGE, "num_blocks %d outside [0, max_blocks_per_req %d]", num_blocks, b->cfg.max_blocks_per_req);
+    if (num_prompt < 0 || num_prompt > num_tokens || num_computed < 0 || num_computed > num_tokens)
+        return fail(RIC_ERANGE, "num_prompt %d / num_computed %d outside [0, %d]", num_prompt, num_computed, num_tokens);
+    if ((num_tokens > 0 && !tokens) || (num_blocks > 0 && !blocks)) return fail(RIC_EINVAL, "payload is NULL");
+    int rc = check_blocks(b, blocks, num_blocks);
+    if (rc) return rc;
+    int32_t row = -1;
+    for (int32_t r = 0; r < b->cfg.max_num_reqs; ++r)
+        if (!b->live[r]) {
+            row = r;
+            break;
+        }
+    if (row < 0) return fail(RIC_EFULL, "no free row (max_num_reqs %d)", b->cfg.max_num_reqs);
+    rc = before_row_overwrite(b, row);
+    if (rc) return rc;
+    rc = stage(b, b->d_tok + (int64_t)row * b->L.tok_stride, tokens, (size_t)num_tokens);
+    if (rc) return rc;
+    rc = stage(b, b->d_blk + (int64_t)row * b->L.blk_stride, blocks, (size_t)num_blocks);
+    if (rc) return rc;
+    const ric_sampling sp = sampling ? *sampling : ric_sampling{1.f, 1.f, 1.f, 0};
+    const int32_t vals[kNumScalarCols] = {num_tokens, num_prompt, num_computed, 0, num_blocks, sp.top_k,
+                                          as_bits(sp.temperature), as_bits(sp.top_p),
+                                          as_bits(sp.repetition_penalty)};
+    for (int c = 0; c < kNumScalarCols; ++c) {
+        b->S(c, row) = vals[c];
+        b->mark(c, row);
+    }
+    b->live[row] = 1;
+    b->req_at[row] = req_id;
+    b->row_of[req_id] = row;
+    b->pending_epoch[row] = b->epoch;
+    ++b->num_live;
+    b->scheduled = false;
+    if (out_row) *out_row = row;
+    return RIC_OK;
+}
+
+int ric_remove_request(ric_batch* b, uint64_t req_id, int32_t* out_row) {
+    if (!b) return fail(RIC_EINVAL, "handle is NULL");
+    int32_t row;
+    int rc = find(b, req_id, &row);
+    if (rc) return rc;
+    b->row_of.erase(req_id);
+    b->live[row] = 0;
+    --b->num_live;
+    b->scheduled = false;
+    if (out_row) *out_row = row;
+    return RIC_OK;
+}
+
+int ric_append_tokens(ric_batch* b, uint64_t req_id, const int32_t* ids, int32_t n) {
+    if (!b) return fail(RIC_EINVAL, "handle is NULL");
+    int32_t row;
+    int rc = find(b, req_id, &row);
+    if (rc) return rc;
+    const int32_t T = b->S(kNumTokens, row);
+    if (n < 0 || (int64_t)T + n > b->cfg.max_model_len)
+        return fail(RIC_EFULL, "row %d: %d + %d tokens exceed max_model_len %d", row, T, n, b->cfg.max_model_len);
+    if (n > 0 && !ids) return fail(RIC_EINVAL, "ids is NULL");
+    rc = stage(b, b->d_tok + (int64_t)row * b->L.tok_stride + T, ids, (size_t)n);
+    if (rc) return rc;
+    b->S(kNumTokens, row) = T + n;
+    b->mark(kNumTokens, row);
+    b->pending_epoch[row] = b->epoch;
+    b->scheduled = false;
+    return RIC_OK;
+}
+
+static int set_blocks(ric_batch* b, uint64_t req_id, const int32_t* ids, int32_t n, bool replace) {
+    if (!b) return fail(RIC_EINVAL, "handle is NULL");
+    int32_t row;
+    int rc = find(b, req_id, &row);
+    if (rc) return rc;
+    const int32_t nb = replace ? 0 : b->S(kNumBlocks, row);
+    if (n < 0 || (int64_t)nb + n > b->cfg.max_blocks_per_req)
+        return fail(RIC_EFULL, "row %d: %d + %d blocks exceed max_blocks_per_req %d", row, nb, n,
+                    b->cfg.max_blocks_per_req);
+    if (n > 0 && !ids) return fail(RIC_EINVAL, "ids is NULL");
+    rc = check_blocks(b, ids, n);
+    if (rc) return rc;
+    if (replace) {
+        rc = before_row_overwrite(b, row);
+        if (rc) return rc;
+    }
+    rc = stage(b, b->d_blk + (int64_t)row * b->L.blk_stride + nb, ids, (size_t)n);
+    if (rc) return rc;
+    b->S(kNumBlocks, row) = nb + n;
+    b->mark(kNumBlocks, row);
+    b->pending_epoch[row] = b->epoch;
+    b->scheduled = false;
+    return RIC_OK;
+}
+
+int ric_append_blocks(ric_batch* b, uint64_t req_id, const int32_t* ids, int32_t n) {
+    return set_blocks(b, req_id, ids, n, false);
+}
+
+int ric_replace_blocks(ric_batch* b, uint64_t req_id, const int32_t* ids, int32_t n) {
+    return set_blocks(b, req_id, ids, n, true);
+}
+
+int32_t ric_condense_plan(const uint8_t* live, int32_t num_rows, int32_t* holes, int32_t* sources) {
+    if (!live || num_rows < 0) return RIC_EINVAL;
+    int32_t lo = 0, hi = num_rows - 1, k = 0;
+    for (;;) {
+        while (lo < num_rows && live[lo]) ++lo;     // next hole from the bottom
+        while (hi >= 0 && !live[hi]) --hi;          // next live row from the top
+        if (lo >= num_rows || hi < 0 || lo >= hi) break;
+        if (holes) holes[k] = lo;
+        if (sources) sources[k] = hi;
+        ++k;
+        ++lo;
+        --hi;
+    }
+    return k;
+}
+
+int ric_condense(ric_batch* b, int32_t* out_num_moved) {
+    if (!b) return fail(RIC_EINVAL, "handle is NULL");
+    const int MR = b->cfg.max_num_reqs;
+    std::vector<int32_t> holes(MR), srcs(MR);
+    const int32_t np = ric_condense_plan(b->live.data(), MR, holes.data(), srcs.data());
+    if (np > 0) {
+        // The pair list rides in the log with any staged deltas; the flush
+        // applies them all before the move kernel runs on the same stream.
+        std::vector<int32_t> pairs(2 * (size_t)np);
+        int32_t max_T = 0;
+        for (int32_t k = 0; k < np; ++k) {
+            pairs[2 * k] = holes[k];
+            pairs[2 * k + 1] = srcs[k];
+            max_T = std::max(max_T, b->S(kNumTokens, srcs[k]));
+        }
+        int rc = stage(b, b->d_pairs, pairs.data(), pairs.size());
+        if (rc) return rc;
+        rc = flush(b);
+        if (rc) return rc;
+        MoveParams mp{};
+        mp.pairs = b->d_pairs;
+        mp.tokens = b->d_tok;
+        mp.blocks = b->d_blk;
+        mp.scal = b->d_scal;
+        mp.tok_stride = b->L.tok_stride;
+        mp.blk_stride = b->L.blk_stride;
+        mp.max_num_reqs = MR;
+        mp.num_pairs = np;
+        mp.chunk_vec4 = 1024;  // 16 KiB of history per workgroup
+        const int chunks = (int)(((int64_t)max_T + 4 * mp.chunk_vec4 - 1) / (4 * mp.chunk_vec4));
+        HIP_TRY(launch_move_rows(mp, chunks, b->stream));
+        for (int32_t k = 0; k < np; ++k) {
+            const int32_t h = holes[k], s = srcs[k];
+            for (int c = 0; c < kNumScalarCols; ++c) b->S(c, h) = b->S(c, s);
+            b->live[h] = 1;
+            b->live[s] = 0;
+            b->req_at[h] = b->req_at[s];
+            b->row_of[b->req_at[h]] = h;
+        }
+    }
+    b->scheduled = false;
+    if (out_num_moved) *out_num_moved = np;
+    return RIC_OK;
+}
+
+int ric_flush(ric_batch* b) {
+    if (!b) return fail(RIC_EINVAL, "handle is NULL");
+    return flush(b);
+}
+
+int32_t ric_num_reqs(const ric_batch* b) { return b ? b->num_live : RIC_EINVAL; }
+
+int32_t ric_row_of(const ric_batch* b, uint64_t req_id) {
+    if (!b) return RIC_EINVAL;
+    auto it = b->row_of.find(req_id);
+    return it == b->row_of.end() ? RIC_ENOENT : it->second;
+}
+
+int ric_req_at(const ric_batch* b, int32_t row, uint64_t* out_req_id) {
+    if (!b || !out_req_id) return fail(RIC_EINVAL, "NULL argument");
+    if (row < 0 || row >= b->cfg.max_num_reqs) return fail(RIC_ERANGE, "row %d out of range", row);
+    if (!b->live[row]) return RIC_ENOENT;
+    *out_req_id = b->req_at[row];
+    return RIC_OK;
+}
+
+int ric_get_columns(const ric_batch* b, ric_columns* o) {
+    if (!b || !o) return fail(RIC_EINVAL, "NULL argument");
+    ric_batch* m = const_cast<ric_batch*>(b);
+    o->tokens = m->d_tok;
+    o->blocks = m->d_blk;
+    o->token_stride = b->L.tok_stride;
+    o->block_stride = b->L.blk_stride;
+    o->num_tokens = m->dcol(kNumTokens);
+    o->num_prompt = m->dcol(kNumPrompt);
+    o->num_computed = m->dcol(kNumComputed);
+    o->num_scheduled = m->dcol(kNumScheduled);
+    o->num_blocks = m->dcol(kNumBlocks);
+    o->top_k = m->dcol(kTopK);
+    o->temperature = reinterpret_cast<float*>(m->dcol(kTemperature));
+    o->top_p = reinterpret_cast<float*>(m->dcol(kTopP));
+    o->repetition_penalty = reinterpret_cast<float*>(m->dcol(kRepPenalty));
+    return RIC_OK;
+}
+
+int ric_sync(ric_batch* b) {
+    if (!b) return fail(RIC_EINVAL, "handle is NULL");
+    HIP_TRY(hipStreamSynchronize(b->stream));
+    return RIC_OK;
+}
+
+int ric_check_step(const ric_config* cfg, int32_t R, const int32_t* c, const int32_t* q, const int32_t* P,
+                   const int32_t* T, const int32_t* nb, int32_t n_pad, ric_step* out) {
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if (R > 0 && (!P || !T || !nb)) return fail(RIC_EINVAL, "row arrays are NULL");
+    int32_t N, mq, ms, ns;
+    rc = check_step_rows(*cfg, R, c, q, P, T, nb, &N, &mq, &ms, &ns);
+    if (rc) return rc;
+    if (n_pad < N || n_pad > cfg->max_num_batched_tokens)
+        return fail(RIC_EINVAL, "num_tokens_padded %d outside [N=%d, max_num_batched_tokens=%d]", n_pad, N,
+                    cfg->max_num_batched_tokens);
+    if (out) {
+        memset(out, 0, sizeof *out);
+        out->num_reqs = R;
+        out->num_actual_tokens = N;
+        out->num_tokens_padded = n_pad;
+        out->max_query_len = mq;
+        out->max_seq_len = ms;
+        out->num_sampled = ns;
+    }
+    return RIC_OK;
+}
+
+int ric_schedule(ric_batch* b, int32_t R, const int32_t* c, const int32_t* q) {
+    if (!b) return fail(RIC_EINVAL, "handle is NULL");
+    if (R != b->num_live) return fail(RIC_EINVAL, "num_reqs %d but %d requests are live", R, b->num_live);
+    if (b->used_rows() != R) return fail(RIC_ESTATE, "rows are not condensed: live rows must be [0, %d)", R);
+    const int MR = b->cfg.max_num_reqs;
+    int32_t N, mq, ms, ns;
+    int rc = check_step_rows(b->cfg, R, c, q, &b->scal[(size_t)kNumPrompt * MR], &b->scal[(size_t)kNumTokens * MR],
+                             &b->scal[(size_t)kNumBlocks * MR], &N, &mq, &ms, &ns);
+    if (rc) return rc;
+    for (int32_t i = 0; i < R; ++i) {
+        b->S(kNumComputed, i) = c[i];
+        b->S(kNumScheduled, i) = q[i];
+    }
+    if (R > 0) {
+        b->mark(kNumComputed, 0);
+        b->mark(kNumComputed, R - 1);
+        b->mark(kNumScheduled, 0);
+        b->mark(kNumScheduled, R - 1);
+    }
+    b->scheduled = true;
+    b->sched_R = R;
+    b->sched_N = N;
+    b->sched_max_q = mq;
+    b->sched_max_seq = ms;
+    b->sched_sampled = ns;
+    return RIC_OK;
+}
+
+int ric_compile(ric_batch* b, int32_t n_pad, ric_step* out) {
+    if (!b) return fail(RIC_EINVAL, "handle is NULL");
+    if (!b->scheduled) return fail(RIC_ESTATE, "ric_schedule must follow the last row change");
+    if (n_pad < b->sched_N || n_pad > b->cfg.max_num_batched_tokens)
+        return fail(RIC_EINVAL, "num_tokens_padded %d outside [N=%d, max_num_batched_tokens=%d]", n_pad,
+                    b->sched_N, b->cfg.max_num_batched_tokens);
+    int rc = flush(b);
+    if (rc) return rc;
+    CompileParams p{};
+    p.scal = b->d_scal;
+    p.tokens = b->d_tok;
+    p.blocks = b->d_blk;
+    p.tok_stride = b->L.tok_stride;
+    p.blk_stride = b->L.blk_stride;
+    p.max_num_reqs = b->cfg.max_num_reqs;
+    p.num_reqs = b->sched_R;
+    p.n_pad = n_pad;
+    p.block_size = b->cfg.block_size;
+    p.block_shift = ilog2_exact(b->cfg.block_size);
+    p.null_slot = b->cfg.null_block * b->cfg.block_size;
+    p.num_token_tiles = (n_pad + kCompileTile - 1) / kCompileTile;
+    p.input_ids = b->d_ids;
+    p.positions = b->d_pos;
+    p.req_indices = b->d_req;
+    p.slot_mapping = b->d_slot;
+    p.query_start_loc = b->d_qsl;
+    p.seq_lens = b->d_seq;
+    p.logits_indices = b->d_logits;
+    p.discard = b->d_discard;
+    p.sample_indices = b->d_sample;
+    p.dev_scalars = b->d_dscal;
+    HIP_TRY(launch_compile(p, b->stream));
+    if (out) {
+        out->input_ids = b->d_ids;
+        out->positions = b->d_pos;
+        out->req_indices = b->d_req;
+        out->slot_mapping = b->d_slot;
+        out->query_start_loc = b->d_qsl;
+        out->seq_lens = b->d_seq;
+        out->logits_indices = b->d_logits;
+        out->discard = b->d_discard;
+        out->sample_indices = b->d_sample;
+        out->dev_scalars = b->d_dscal;
+        out->num_reqs = b->sched_R;
+        out->num_actual_tokens = b->sched_N;
+        out->num_tokens_padded = n_pad;
+        out->max_query_len = b->sched_max_q;
+        out->max_seq_len = b->sched_max_seq;
+        out->num_sampled = b->sched_sampled;
+    }
+    return RIC_OK;
+}
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+int ric_reshape_and_cache(const void* const* k, const void* const* v, void* const* k_cache, void* const* v_cache,
+                          int32_t num_layers, const int32_t* slot_mapping, int32_t num_tokens,
+                          int64_t src_row_stride, int32_t row_bytes, int64_t num_slots, int32_t* dev_status,
+                          void* stream) {
+    if (num_layers < 0 || num_tokens < 0) return fail(RIC_EINVAL, "negative count");
+    if (num_layers == 0 || num_tokens == 0) return RIC_OK;
+    if (!k || !v || !k_cache || !v_cache || !slot_mapping) return fail(RIC_EINVAL, "NULL pointer argument");
+    if (row_bytes <= 0 || row_bytes % 16 != 0) return fail(RIC_EINVAL, "row_bytes %d not a positive multiple of 16", row_bytes);
+    if (src_row_stride == 0) src_row_stride = row_bytes;
+    if (src_row_stride < row_bytes || src_row_stride % 16 != 0)
+        return fail(RIC_EINVAL, "src_row_stride %lld must be a multiple of 16 and >= row_bytes", (long long)src_row_stride);
+    if (num_slots <= 0) return fail(RIC_EINVAL, "num_slots must be positive");
+    for (int32_t l = 0; l < num_layers; ++l)
+        if (!k[l] || !v[l] || !k_cache[l] || !v_cache[l] || !aligned16(k[l]) || !aligned16(v[l]) ||
+            !aligned16(k_cache[l]) || !aligned16(v_cache[l]))
+            return fail(RIC_EINVAL, "layer %d: NULL or misaligned pointer", l);
+    KVParams p{};
+    p.slot = slot_mapping;
+    p.src_stride = src_row_stride;
+    p.num_slots = num_slots;
+    p.status = dev_status;
+    p.num_tokens = num_tokens;
+    p.row_bytes = row_bytes;
+    p.chunk_shift = ilog2_exact(row_bytes / 16);
+    p.rows_per_wg = 0;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int32_t l0 = 0; l0 < num_layers; l0 += kMaxLayersPerLaunch) {
+        const int nl = std::min<int>(kMaxLayersPerLaunch, num_layers - l0);
+        for (int i = 0; i < nl; ++i) {
+            p.k[i] = static_cast<const uint8_t*>(k[l0 + i]);
+            p.v[i] = static_cast<const uint8_t*>(v[l0 + i]);
+            p.kc[i] = static_cast<uint8_t*>(k_cache[l0 + i]);
+            p.vc[i] = static_cast<uint8_t*>(v_cache[l0 + i]);
+        }
+        HIP_TRY(launch_kv_scatter(p, nl, s));
+    }
+    return RIC_OK;
+}
+
+int ric_gather_rows(const void* src, int64_t src_row_stride, int64_t src_rows, const int32_t* idx,
+                    const int32_t* dev_count, int32_t max_rows, int32_t row_bytes, void* dst,
+                    int64_t dst_row_stride, int32_t* dev_status, void* stream) {
+    if (max_rows < 0) return fail(RIC_EINVAL, "max_rows negative");
+    if (max_rows == 0) return RIC_OK;
+    if (!src || !idx || !dst) return fail(RIC_EINVAL, "NULL pointer argument");
+    if (row_bytes <= 0 || row_bytes % 16 != 0) return fail(RIC_EINVAL, "row_bytes %d not a positive multiple of 16", row_bytes);
+    if (src_row_stride == 0) src_row_stride = row_bytes;
+    if (dst_row_stride == 0) dst_row_stride = row_bytes;
+    if (src_row_stride < row_bytes || dst_row_stride < row_bytes || src_row_stride % 16 || dst_row_stride % 16)
+        return fail(RIC_EINVAL, "strides must be multiples of 16 and >= row_bytes");
+    if (!aligned16(src) || !aligned16(dst)) return fail(RIC_EINVAL, "src/dst must be 16-byte aligned");
+    if (src_rows < 0) return fail(RIC_EINVAL, "src_rows negative");
+    GatherParams p{};
+    p.src = static_cast<const uint8_t*>(src);
+    p.src_stride = src_row_stride;
+    p.src_rows = src_rows;
+    p.idx = idx;
+    p.dev_count = dev_count;
+    p.dst = static_cast<uint8_t*>(dst);
+    p.dst_stride = dst_row_stride;
+    p.status = dev_status;
+    p.max_rows = max_rows;
+    p.row_bytes = row_bytes;
+    HIP_TRY(launch_gather(p, static_cast<hipStream_t>(stream)));
+    return RIC_OK;
+}
+
+int32_t ric_padded_size(const int32_t* sizes, int32_t n, int32_t num_tokens) {
+    if (num_tokens < 0 || n < 0 || (n > 0 && !sizes)) return RIC_EINVAL;
+    int32_t best = -1;
+    for (int32_t i = 0; i < n; ++i)
+        if (sizes[i] >= num_tokens && (best < 0 || sizes[i] < best)) best = sizes[i];
+    return best < 0 ? num_tokens : best;
+}
+
+}  // extern "C"

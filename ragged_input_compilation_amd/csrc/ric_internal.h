@@ -1,0 +1,112 @@
+// Internal declarations shared by the host control plane and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ric {
+
+// Per-row scalar columns of the column store, in this order in one
+// [kNumScalarCols][max_num_reqs] int32 region (float columns hold their bits).
+enum ScalarCol : int {
+    kNumTokens = 0,
+    kNumPrompt = 1,
+    kNumComputed = 2,
+    kNumScheduled = 3,
+    kNumBlocks = 4,
+    kTopK = 5,
+    kTemperature = 6,
+    kTopP = 7,
+    kRepPenalty = 8,
+    kNumScalarCols = 9
+};
+
+constexpr int kMaxReqsLimit = 8000;       // compile LDS: (2R + 5) int32 per workgroup < 64 KiB
+constexpr int kMaxLayersPerLaunch = 32;   // K/V pointer sets passed by value
+constexpr int kNumDevScalars = 8;
+
+// One staged copy: n_words 32-bit words from the staging payload to dst.
+struct DeltaOp {
+    uint64_t dst;
+    uint32_t src_word;
+    uint32_t n_words;
+};
+
+struct CompileParams {
+    const int32_t* scal;          // [kNumScalarCols][max_num_reqs]
+    const int32_t* tokens;        // [max_num_reqs][tok_stride]
+    const int32_t* blocks;        // [max_num_reqs][blk_stride]
+    int64_t tok_stride;
+    int64_t blk_stride;
+    int32_t max_num_reqs;
+    int32_t num_reqs;
+    int32_t n_pad;
+    int32_t block_size;
+    int32_t block_shift;          // log2(block_size) when a power of two, else -1
+    int32_t null_slot;            // null_block * block_size
+    int32_t num_token_tiles;
+    int32_t* input_ids;
+    int32_t* positions;
+    int32_t* req_indices;
+    int32_t* slot_mapping;
+    int32_t* query_start_loc;
+    int32_t* seq_lens;
+    int32_t* logits_indices;
+    uint8_t* discard;
+    int32_t* sample_indices;
+    int32_t* dev_scalars;
+};
+
+struct KVParams {
+    const uint8_t* k[kMaxLayersPerLaunch];
+    const uint8_t* v[kMaxLayersPerLaunch];
+    uint8_t* kc[kMaxLayersPerLaunch];
+    uint8_t* vc[kMaxLayersPerLaunch];
+    const int32_t* slot;
+    int64_t src_stride;
+    int64_t num_slots;
+    int32_t* status;
+    int32_t num_tokens;
+    int32_t row_bytes;
+    int32_t chunk_shift;          // log2(row_bytes / 16) when a power of two, else -1
+    int32_t rows_per_wg;
+};
+
+struct GatherParams {
+    const uint8_t* src;
+    int64_t src_stride;
+    int64_t src_rows;
+    const int32_t* idx;
+    const int32_t* dev_count;
+    uint8_t* dst;
+    int64_t dst_stride;
+    int32_t* status;
+    int32_t max_rows;
+    int32_t row_bytes;
+};
+
+struct MoveParams {
+    const int32_t* pairs;         // [num_pairs][2] = (destination hole, source row)
+    int32_t* tokens;
+    int32_t* blocks;
+    int32_t* scal;
+    int64_t tok_stride;
+    int64_t blk_stride;
+    int32_t max_num_reqs;
+    int32_t num_pairs;
+    int32_t chunk_vec4;           // 16-byte units of token history per workgroup
+};
+
+// Launchers (enqueue only; return the launch status).
+hipError_t launch_compile(const CompileParams& p, hipStream_t s);
+hipError_t launch_kv_scatter(const KVParams& p, int num_layers, hipStream_t s);
+hipError_t launch_gather(const GatherParams& p, hipStream_t s);
+hipError_t launch_move_rows(const MoveParams& p, int max_token_chunks, hipStream_t s);
+hipError_t launch_apply_deltas(const uint32_t* payload, const DeltaOp* ops, int n_ops, hipStream_t s);
+
+// Token tile of one compile workgroup.
+constexpr int kCompileThreads = 256;
+constexpr int kCompileTokensPerThread = 1;
+constexpr int kCompileTile = kCompileThreads * kCompileTokensPerThread;
+
+}  // namespace ric

@@ -1,0 +1,360 @@
+// HIP kernels for gfx950 (CDNA4, wave64): step compile, paged K/V write,
+// row gather, condense row move and staged-delta apply.
+//
+// Sources (page title, section):
+//   [P1] "vLLM 源码完全拆解（五）：GPUModelRunner 如何把动态请求拼成一次 GPU 前向"
+//   [P3] "变长批处理与一次混合前向"
+//   [P4] "04 · 模型执行与 CUDA Graph"
+//
+// Nothing here is a contraction, so no MFMA: the compile is a few integer
+// operations per token behind two dependent loads, and the K/V write and the
+// gather are indexed copies bound by HBM bandwidth.  The copies move 16-byte
+// vectors per lane with non-temporal loads and stores (each byte is touched
+// once per step), keep several loads in flight per lane before storing, and
+// use 64-bit byte offsets.
+#include "ric_internal.h"
+
+namespace ric {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+namespace {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int y = __shfl_up(x, d, kWave);
+        if (lane >= d) x += y;
+    }
+    return x;
+}
+
+__device__ __forceinline__ int wave_max(int x) {
+#pragma unroll
+    for (int d = kWave / 2; d > 0; d >>= 1) x = max(x, __shfl_xor(x, d, kWave));
+    return x;
+}
+
+// Exclusive scan of one value per thread across the workgroup; *total gets
+// the sum.  `tmp` holds one int per wave.  Contains barriers: every thread of
+// the workgroup must call it.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int x, int* tmp, int* total) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = threadIdx.x / kWave;
+    const int inc = wave_inclusive_scan(x);
+    if (lane == kWave - 1) tmp[wid] = inc;
+    __syncthreads();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NT / kWave; ++w) {
+        const int v = tmp[w];
+        off += (w < wid) ? v : 0;
+        tot += v;
+    }
+    __syncthreads();
+    *total = tot;
+    return off + inc - x;
+}
+
+template <int NT>
+__device__ __forceinline__ int block_max(int x, int* tmp) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = threadIdx.x / kWave;
+    x = wave_max(x);
+    if (lane == 0) tmp[wid] = x;
+    __syncthreads();
+    int m = tmp[0];
+#pragma unroll
+    for (int w = 1; w < NT / kWave; ++w) m = max(m, tmp[w]);
+    __syncthreads();
+    return m;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Step compile.  Workgroups 0..num_token_tiles-1 each own a tile of the flat
+// token stream; the last workgroup writes the per-request outputs.  Every
+// workgroup first rebuilds query_start_loc in LDS from the scheduled counts
+// (R <= 8000), so one launch needs no grid-wide synchronisation.
+//   query_start_loc: exclusive prefix sum of q       [P1 §第一步]
+//   position of token j of request i: c_i + j        [P1 §第二步]
+//   input id: token table row i at that position     [P1 §第三步]
+//   slot: block_table[i][p / B] * B + p % B          [P1 §Block table 是逐请求的页表]
+//   logits index: qsl[i+1] - 1; partial prefills discarded  [P1 §第四步], [P1 §Chunked Prefill]
+//   padded tokens -> null block                      [P1 §固定地址与动态有效长度如何共存], [P4 §5]
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kCompileThreads) void compile_kernel(CompileParams p) {
+    extern __shared__ int32_t smem[];
+    const int R = p.num_reqs;
+    int32_t* s_qsl = smem;               // [R + 1]
+    int32_t* s_base = smem + R + 1;      // [R]: c_i - qsl_i, so position = base + t
+    int32_t* s_tmp = s_base + R;         // [kCompileThreads / kWave]
+
+    const int tid = threadIdx.x;
+    const int32_t* col_c = p.scal + (int64_t)kNumComputed * p.max_num_reqs;
+    const int32_t* col_q = p.scal + (int64_t)kNumScheduled * p.max_num_reqs;
+    const int32_t* col_P = p.scal + (int64_t)kNumPrompt * p.max_num_reqs;
+
+    // Scan of q: each thread owns a contiguous run of requests.
+    const int per = (R + kCompileThreads - 1) / kCompileThreads;
+    const int r0 = min(R, tid * per);
+    const int r1 = min(R, r0 + per);
+    int local = 0;
+    for (int i = r0; i < r1; ++i) {
+        const int q = col_q[i];
+        s_qsl[i] = q;
+        local += q;
+    }
+    int N = 0;
+    int run = block_exclusive_scan<kCompileThreads>(local, s_tmp, &N);
+    for (int i = r0; i < r1; ++i) {
+        const int q = s_qsl[i];
+        s_qsl[i] = run;
+        s_base[i] = col_c[i] - run;
+        run += q;
+    }
+    if (tid == 0) s_qsl[R] = N;
+    __syncthreads();
+
+    if ((int)blockIdx.x < p.num_token_tiles) {
+        const int tile0 = blockIdx.x * kCompileTile;
+#pragma unroll
+        for (int k = 0; k < kCompileTokensPerThread; ++k) {
+            const int t = tile0 + k * kCompileThreads + tid;
+            if (t >= p.n_pad) break;
+            if (t < N) {
+                // request r: the last one whose interval starts at or before t
+                int lo = 0, hi = R - 1;
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (s_qsl[mid] <= t) lo = mid; else hi = mid - 1;
+                }
+                const int r = lo;
+                const int pos = s_base[r] + t;
+                int lb, off;
+                if (p.block_shift >= 0) {
+                    lb = pos >> p.block_shift;
+                    off = pos & (p.block_size - 1);
+                } else {
+                    lb = pos / p.block_size;
+                    off = pos - lb * p.block_size;
+                }
+                p.positions[t] = pos;
+                p.req_indices[t] = r;
+                // The host validated c + q <= T and the block count; this guard
+                // only keeps a corrupted column from turning into a wild read.
+                if (pos >= 0 && pos < p.tok_stride && lb < p.blk_stride) {
+                    p.input_ids[t] = p.tokens[(int64_t)r * p.tok_stride + pos];
+                    p.slot_mapping[t] = p.blocks[(int64_t)r * p.blk_stride + lb] * p.block_size + off;
+                } else {
+                    p.input_ids[t] = -1;
+                    p.slot_mapping[t] = p.null_slot;
+                    atomicAdd(p.dev_scalars + 6, 1);
+                }
+            } else {
+                p.input_ids[t] = 0;
+                p.positions[t] = 0;
+                p.req_indices[t] = -1;
+                p.slot_mapping[t] = p.null_slot;
+            }
+        }
+        return;
+    }
+
+    // Per-request outputs (one workgroup).
+    const int MR = p.max_num_reqs;
+    int max_q = 0, max_seq = 0, kept = 0;
+    for (int i = r0; i < r1; ++i) {
+        const int q = s_qsl[i + 1] - s_qsl[i];
+        const int seq = s_base[i] + s_qsl[i] + q;   // c_i + q_i
+        max_q = max(max_q, q);
+        max_seq = max(max_seq, seq);
+        kept += (seq >= col_P[i]) ? 1 : 0;
+    }
+    int num_sampled = 0;
+    int slot_out = block_exclusive_scan<kCompileThreads>(kept, s_tmp, &num_sampled);
+    max_q = block_max<kCompileThreads>(max_q, s_tmp);
+    max_seq = block_max<kCompileThreads>(max_seq, s_tmp);
+    for (int i = r0; i < r1; ++i) {
+        const int seq = s_base[i] + s_qsl[i + 1];
+        const int li = s_qsl[i + 1] - 1;
+        const bool part = seq < col_P[i];
+        p.seq_lens[i] = seq;
+        p.logits_indices[i] = li;
+        p.discard[i] = part ? 1 : 0;
+        if (!part) p.sample_indices[slot_out++] = li;
+    }
+    for (int i = tid; i <= MR; i += kCompileThreads) {
+        p.query_start_loc[i] = (i <= R) ? s_qsl[i] : N;
+        if (i >= R && i < MR) {
+            p.seq_lens[i] = 0;
+            p.logits_indices[i] = -1;
+            p.discard[i] = 1;
+        }
+        if (i >= num_sampled && i < MR) p.sample_indices[i] = -1;
+    }
+    if (tid == 0) {
+        p.dev_scalars[0] = R;
+        p.dev_scalars[1] = N;
+        p.dev_scalars[2] = p.n_pad;
+        p.dev_scalars[3] = max_q;
+        p.dev_scalars[4] = max_seq;
+        p.dev_scalars[5] = num_sampled;
+    }
+}
+
+hipError_t launch_compile(const CompileParams& p, hipStream_t s) {
+    const size_t lds = sizeof(int32_t) * (2 * (size_t)p.num_reqs + 1 + kCompileThreads / kWave);
+    hipLaunchKernelGGL(compile_kernel, dim3(p.num_token_tiles + 1), dim3(kCompileThreads), lds, s, p);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Paged K/V write: row t of every K and V source goes to cache row slot[t]
+// ([P1 §3. 物理 KV 槽位]; [P3 §实现]).  blockIdx.y = 2*layer + (K:0, V:1);
+// blockIdx.x = a run of rows_per_wg token rows.  Lanes walk the run's 16-byte
+// chunks in order, so both the read of a source row and the write of a cache
+// row are contiguous; U chunks per lane are loaded before any is stored.
+// ---------------------------------------------------------------------------
+template <int U>
+__global__ __launch_bounds__(256) void kv_scatter_kernel(KVParams p) {
+    const int tensor = blockIdx.y;
+    const int layer = tensor >> 1;
+    const bool is_v = (tensor & 1) != 0;
+    const uint8_t* __restrict__ src = is_v ? p.v[layer] : p.k[layer];
+    uint8_t* __restrict__ dst = is_v ? p.vc[layer] : p.kc[layer];
+    const int t0 = blockIdx.x * p.rows_per_wg;
+    const int rows = min(p.rows_per_wg, p.num_tokens - t0);
+    const int C = p.row_bytes >> 4;
+    const int total = rows * C;
+    for (int base = threadIdx.x; base < total; base += 256 * U) {
+        u32x4 val[U];
+        int64_t doff[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = base + u * 256;
+            doff[u] = -1;
+            if (i < total) {
+                const int r = (p.chunk_shift >= 0) ? (i >> p.chunk_shift) : (i / C);
+                const int j = i - r * C;
+                const int t = t0 + r;
+                const int s = p.slot[t];
+                val[u] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4*>(src + (int64_t)t * p.src_stride + ((int64_t)j << 4)));
+                if (s >= 0 && (int64_t)s < p.num_slots)
+                    doff[u] = (int64_t)s * p.row_bytes + ((int64_t)j << 4);
+                else if (j == 0 && p.status != nullptr)
+                    atomicAdd(p.status, 1);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (doff[u] >= 0) __builtin_nontemporal_store(val[u], reinterpret_cast<u32x4*>(dst + doff[u]));
+    }
+}
+
+constexpr int kKvUnroll = 4;
+constexpr int kKvChunksPerWg = 256 * kKvUnroll;   // 16 KiB per workgroup
+
+hipError_t launch_kv_scatter(const KVParams& p_in, int num_layers, hipStream_t s) {
+    KVParams p = p_in;
+    const int C = p.row_bytes >> 4;
+    p.rows_per_wg = p.rows_per_wg > 0 ? p.rows_per_wg : (kKvChunksPerWg / C > 0 ? kKvChunksPerWg / C : 1);
+    const int gx = (p.num_tokens + p.rows_per_wg - 1) / p.rows_per_wg;
+    if (gx == 0) return hipSuccess;
+    hipLaunchKernelGGL(kv_scatter_kernel<kKvUnroll>, dim3(gx, 2 * num_layers), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Row gather: dst[m] = src[idx[m]] for m < count (hidden states at the logits
+// rows; [P1 §第四步]).  One workgroup per output row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void gather_kernel(GatherParams p) {
+    const int m = blockIdx.x;
+    int count = p.max_rows;
+    if (p.dev_count != nullptr) count = min(count, *p.dev_count);
+    if (m >= count) return;
+    int64_t id = p.idx[m];
+    if (id >= p.src_rows) {
+        if (threadIdx.x == 0 && p.status != nullptr) atomicAdd(p.status, 1);
+        id = -1;
+    }
+    const int C = p.row_bytes >> 4;
+    u32x4* out = reinterpret_cast<u32x4*>(p.dst + (int64_t)m * p.dst_stride);
+    if (id < 0) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        for (int j = threadIdx.x; j < C; j += 256) out[j] = z;
+        return;
+    }
+    const u32x4* in = reinterpret_cast<const u32x4*>(p.src + id * p.src_stride);
+    for (int j = threadIdx.x; j < C; j += 256) out[j] = __builtin_nontemporal_load(in + j);
+}
+
+hipError_t launch_gather(const GatherParams& p, hipStream_t s) {
+    if (p.max_rows == 0) return hipSuccess;
+    hipLaunchKernelGGL(gather_kernel, dim3(p.max_rows), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Condense: move every column of source row -> destination hole for each
+// pair ([P1 §行号是一种短生命周期地址]).  Holes and sources are disjoint sets,
+// so all pairs move at once.  blockIdx.y = pair, blockIdx.x = chunk of the
+// token history; chunk 0 also moves the block row and the scalar columns.
+// Row strides are multiples of 4 words, so rows copy in 16-byte units (words
+// past the valid prefix are stale in both rows).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void move_rows_kernel(MoveParams p) {
+    const int pair = blockIdx.y;
+    const int dst_row = p.pairs[2 * pair];
+    const int src_row = p.pairs[2 * pair + 1];
+    const int T = p.scal[(int64_t)kNumTokens * p.max_num_reqs + src_row];
+    const int nvec = min((T + 3) >> 2, (int)(p.tok_stride >> 2));
+    const int v0 = blockIdx.x * p.chunk_vec4;
+    const int v1 = min(nvec, v0 + p.chunk_vec4);
+    const u32x4* ts = reinterpret_cast<const u32x4*>(p.tokens + (int64_t)src_row * p.tok_stride);
+    u32x4* td = reinterpret_cast<u32x4*>(p.tokens + (int64_t)dst_row * p.tok_stride);
+    for (int v = v0 + threadIdx.x; v < v1; v += 256) td[v] = ts[v];
+    if (blockIdx.x == 0) {
+        const int nb = min(p.scal[(int64_t)kNumBlocks * p.max_num_reqs + src_row], (int)p.blk_stride);
+        const u32x4* bs = reinterpret_cast<const u32x4*>(p.blocks + (int64_t)src_row * p.blk_stride);
+        u32x4* bd = reinterpret_cast<u32x4*>(p.blocks + (int64_t)dst_row * p.blk_stride);
+        for (int v = threadIdx.x; v < ((nb + 3) >> 2); v += 256) bd[v] = bs[v];
+        if (threadIdx.x < kNumScalarCols) {
+            const int64_t col = (int64_t)threadIdx.x * p.max_num_reqs;
+            p.scal[col + dst_row] = p.scal[col + src_row];
+        }
+    }
+}
+
+hipError_t launch_move_rows(const MoveParams& p, int max_token_chunks, hipStream_t s) {
+    if (p.num_pairs == 0) return hipSuccess;
+    hipLaunchKernelGGL(move_rows_kernel, dim3(max_token_chunks > 0 ? max_token_chunks : 1, p.num_pairs),
+                       dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Staged deltas: one workgroup per op copies its words from the uploaded
+// payload to the column store.  Ops of one flush never overlap.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void apply_deltas_kernel(const uint32_t* payload, const DeltaOp* ops) {
+    const DeltaOp op = ops[blockIdx.x];
+    uint32_t* dst = reinterpret_cast<uint32_t*>(op.dst);
+    const uint32_t* src = payload + op.src_word;
+    for (uint32_t w = threadIdx.x; w < op.n_words; w += 256) dst[w] = src[w];
+}
+
+hipError_t launch_apply_deltas(const uint32_t* payload, const DeltaOp* ops, int n_ops, hipStream_t s) {
+    if (n_ops == 0) return hipSuccess;
+    hipLaunchKernelGGL(apply_deltas_kernel, dim3(n_ops), dim3(256), 0, s, payload, ops);
+    return hipGetLastError();
+}
+
+}  // namespace ric

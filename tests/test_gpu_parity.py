@@ -1,0 +1,403 @@
+"""GPU parity: libric on an MI355X against the CPU oracle, element by element.
+
+Compile outputs and the column store must be bit-exact; K/V cache rows and
+gathered hidden rows byte-exact.  Small cases are compared in full (every
+cache byte outside the null block); the full-size configurations compare the
+whole compile output and sampled cache rows, plus sentinel checks that nothing
+outside the real slots was written."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import batch as ref_batch, cbind, step as ref_step, vectorised
+from tests.gpu_helpers import assert_step_equal, expected_step, read_rows_i32, replay_history
+
+pytestmark = pytest.mark.gpu
+
+CONFIGS = ["worked_example", "decode_heavy", "mixed", "churn", "long_context", "long_context_forced"]
+
+
+@pytest.fixture(scope="module")
+def rt():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from ragged_input_compilation_amd import _ric, runner
+    return _ric, runner
+
+
+def _compile(rt, w):
+    ric, runner = rt
+    b = runner.Batch(runner.config_of(w))
+    moved = b.load_history(w)
+    ref, order = replay_history(w)
+    assert b.row_order() == order, "row order differs from the reference batch"
+    b.schedule_from(w, order)
+    exp = expected_step(w, ref, use_python=(w.name == "worked_example"))
+    n_pad = ric.ric_padded_size(w.capture_sizes, exp["num_actual_tokens"])
+    assert n_pad == exp["n_pad"]
+    s = b.compile(n_pad)
+    assert (s.num_reqs, s.num_actual_tokens, s.num_tokens_padded, s.max_query_len, s.max_seq_len,
+            s.num_sampled) == (exp["num_reqs"], exp["num_actual_tokens"], n_pad, exp["max_query_len"],
+                               exp["max_seq_len"], exp["num_sampled"])
+    return b, s, ref, order, exp, moved
+
+
+@pytest.mark.parametrize("name", CONFIGS)
+def test_compile_matches_oracle(rt, name):
+    w = workloads.get(name)
+    b, s, ref, order, exp, moved = _compile(rt, w)
+    got = b.step_outputs(s)
+    torch.cuda.synchronize()
+    assert_step_equal(got, exp, name)
+    b.close()
+
+
+def test_worked_example_printed_values(rt):
+    """The configuration built from the third page's example gives its printed
+    query_start_loc, seq_lens and logits indices on the GPU."""
+    w = workloads.get("worked_example")
+    b, s, *_ = _compile(rt, w)
+    got = b.step_outputs(s)
+    assert list(got["query_start_loc"][:4]) == [0, 7, 8, 20]
+    assert list(got["seq_lens"][:3]) == [7, 6, 22]
+    assert list(got["logits_indices"][:3]) == [6, 7, 19]
+    assert list(got["positions"][:20]) == list(range(7)) + [5] + list(range(10, 22))
+    assert s.num_tokens_padded == 32
+    b.close()
+
+
+@pytest.mark.parametrize("name", ["churn", "mixed", "worked_example"])
+def test_column_store_matches_reference_batch(rt, name):
+    """After the history (adds, removals, condense, refills) every live row's
+    columns equal the reference batch's: token history, block row, counters
+    and sampling values moved together."""
+    ric, runner = rt
+    w = workloads.get(name)
+    b, s, ref, order, exp, moved = _compile(rt, w)
+    if name == "churn":
+        assert moved > 0
+    cols = ric.ric_get_columns(b.h)
+    R = len(order)
+    T = b.device_i32(cols.num_tokens, R)
+    P = b.device_i32(cols.num_prompt, R)
+    C = b.device_i32(cols.num_computed, R)
+    Q = b.device_i32(cols.num_scheduled, R)
+    NB = b.device_i32(cols.num_blocks, R)
+    K = b.device_i32(cols.top_k, R)
+    temp = b.device_u8(cols.temperature, 4 * R).view(np.float32)
+    top_p = b.device_u8(cols.top_p, 4 * R).view(np.float32)
+    rep = b.device_u8(cols.repetition_penalty, 4 * R).view(np.float32)
+    for i in range(R):
+        r = ref.rows[i]
+        assert (T[i], P[i], C[i], Q[i], NB[i]) == (len(r.tokens), r.num_prompt, r.num_computed,
+                                                   r.num_scheduled, len(r.blocks)), f"row {i}"
+        t_, p_, rp_, k_ = r.sampling
+        assert (temp[i], top_p[i], rep[i], K[i]) == (np.float32(t_), np.float32(p_), np.float32(rp_), k_)
+    for i in range(R):
+        r = ref.rows[i]
+        toks = read_rows_i32(b.workspace, cols.tokens, cols.token_stride, [i], len(r.tokens))[0]
+        assert np.array_equal(toks, np.asarray(r.tokens, np.int32)), f"token row {i}"
+        blks = read_rows_i32(b.workspace, cols.blocks, cols.block_stride, [i], len(r.blocks))[0]
+        assert np.array_equal(blks, np.asarray(r.blocks, np.int32)), f"block row {i}"
+    b.close()
+
+
+def _full_kv_check(rt, w, b, s, exp, layers=None):
+    """Every cache byte: real slots equal their source rows, everything outside
+    the real slots and the null block keeps its sentinel."""
+    ric, runner = rt
+    L = w.num_layers if layers is None else layers
+    n_pad = exp["n_pad"]
+    kc, vc = runner.alloc_caches(w, L, fill=0x3A5C)
+    k, v = runner.alloc_sources(w, n_pad, seed=w.seed + 11, num_layers=L, host=True)
+    kv = runner.KVSet(k, v, kc, vc, w.row_bytes, w.num_kv_blocks * w.block_size)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    runner.reshape_and_cache(kv, s.slot_mapping, n_pad, dev_status=status.data_ptr())
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    rows = w.num_kv_blocks * w.block_size
+    B = w.block_size
+    slots = exp["slot_mapping"]
+    for l in range(L):
+        for src, cache in ((k[l], kc[l]), (v[l], vc[l])):
+            want = np.full((rows, w.row_bytes // 2), 0x3A5C, np.int16)
+            vectorised.reshape_and_cache(src.view(torch.int16).reshape(n_pad, -1).cpu().numpy(),
+                                         src.view(torch.int16).reshape(n_pad, -1).cpu().numpy(),
+                                         want, want.copy(), slots)
+            got = cache.view(torch.int16).reshape(rows, -1).cpu().numpy()
+            assert np.array_equal(got[B:], want[B:]), f"layer {l}: cache differs outside the null block"
+
+
+def test_kv_write_worked_example_full(rt):
+    w = workloads.get("worked_example")
+    b, s, ref, order, exp, _ = _compile(rt, w)
+    _full_kv_check(rt, w, b, s, exp)
+    b.close()
+
+
+@pytest.mark.parametrize("name", ["decode_heavy", "mixed", "churn", "long_context"])
+def test_kv_write_full_size_sampled(rt, name):
+    """Full-size caches, every layer of the configuration, one launch: sampled
+    real tokens (plus every token of up to 2048) are compared with their source
+    rows at the oracle's slot, and sampled slots outside the step keep their
+    sentinel."""
+    ric, runner = rt
+    w = workloads.get(name)
+    b, s, ref, order, exp, _ = _compile(rt, w)
+    n_pad, N = exp["n_pad"], exp["num_actual_tokens"]
+    kc, vc = runner.alloc_caches(w, fill=0x1F2E)
+    k, v = runner.alloc_sources(w, n_pad, seed=w.seed + 17)
+    kv = runner.KVSet(k, v, kc, vc, w.row_bytes, w.num_kv_blocks * w.block_size)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    runner.reshape_and_cache(kv, s.slot_mapping, n_pad, dev_status=status.data_ptr())
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    rng = np.random.default_rng(5)
+    toks = np.arange(N) if N <= 2048 else np.sort(rng.choice(N, 2048, replace=False))
+    slots = exp["slot_mapping"][toks]
+    real = set(exp["slot_mapping"][:N].tolist())
+    B = w.block_size
+    nslots = w.num_kv_blocks * B
+    free = rng.integers(B, nslots, size=4096)
+    free = np.array([x for x in free if int(x) not in real][:2048])
+    t_idx = torch.from_numpy(toks).cuda()
+    s_idx = torch.from_numpy(slots).cuda()
+    f_idx = torch.from_numpy(free).cuda()
+    for l in range(w.num_layers):
+        for src, cache in ((k[l], kc[l]), (v[l], vc[l])):
+            flat = cache.view(torch.int16).reshape(nslots, -1)
+            srcf = src.view(torch.int16).reshape(n_pad, -1)
+            assert torch.equal(flat[s_idx], srcf[t_idx]), f"layer {l}: sampled rows differ"
+            assert bool((flat[f_idx] == 0x1F2E).all()), f"layer {l}: a slot outside the step was written"
+    del kc, vc, k, v, kv
+    torch.cuda.empty_cache()
+    b.close()
+
+
+@pytest.mark.parametrize("name", CONFIGS)
+def test_gather_matches_oracle(rt, name):
+    """Hidden rows gathered at logits_indices (one per request) and at the
+    compacted sample_indices with the device count."""
+    ric, runner = rt
+    w = workloads.get(name)
+    b, s, ref, order, exp, _ = _compile(rt, w)
+    n_pad, R, MR = exp["n_pad"], exp["num_reqs"], w.max_num_reqs
+    g = torch.Generator(device="cuda")
+    g.manual_seed(w.seed + 23)
+    hidden = torch.randn((n_pad, w.hidden_size), generator=g, device="cuda").to(torch.bfloat16)
+    out = torch.full((MR, w.hidden_size), 7.0, dtype=torch.bfloat16, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    runner.gather(hidden, s.logits_indices, 0, R, out, dev_status=status.data_ptr())
+    out2 = torch.full((MR, w.hidden_size), 7.0, dtype=torch.bfloat16, device="cuda")
+    runner.gather(hidden, s.sample_indices, s.dev_scalars + 20, MR, out2, dev_status=status.data_ptr())
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    li = torch.from_numpy(exp["logits_indices"][:R]).cuda()
+    assert torch.equal(out[:R].view(torch.int16), hidden[li].view(torch.int16))
+    assert bool((out[R:] == 7.0).all())
+    ns = exp["num_sampled"]
+    si = torch.from_numpy(exp["sample_indices"][:ns]).cuda()
+    assert torch.equal(out2[:ns].view(torch.int16), hidden[si].view(torch.int16))
+    assert bool((out2[ns:] == 7.0).all())
+    b.close()
+
+
+def _tiny_workload(rng, B, R, max_q=6, max_c=20, extra_pad=3):
+    reqs = workloads.random_batch(rng, num_reqs=R, block_size=B, max_model_len=64, num_kv_blocks=200,
+                                  max_q=max_q, max_c=max_c)
+    N = sum(r.num_scheduled for r in reqs)
+    w = workloads.Workload("tiny", block_size=B, max_num_reqs=R + int(rng.integers(0, 3)), max_model_len=64,
+                           max_blocks_per_req=64, max_num_batched_tokens=N + extra_pad, num_kv_blocks=200,
+                           kv_heads=1, head_dim=8 * int(rng.integers(1, 5)), kv_dtype="f16", num_layers=2,
+                           hidden_size=64, gather="all", initial=reqs,
+                           capture_sizes=[N + int(rng.integers(0, extra_pad + 1))], seed=int(rng.integers(1 << 30)))
+    return w
+
+
+def test_bruteforce_tiny_batches(rt):
+    """Many tiny random batches, block sizes 1, 2, 3, 4, 8 and 16, padded
+    sizes above N: every compile output and every cache byte (outside the null
+    block) equals the oracle."""
+    ric, runner = rt
+    rng = np.random.default_rng(77)
+    for trial in range(120):
+        B = int(rng.choice([1, 2, 3, 4, 8, 16]))
+        R = int(rng.integers(1, 6))
+        w = _tiny_workload(rng, B, R)
+        b, s, ref, order, exp, _ = _compile(rt, w)
+        assert_step_equal(b.step_outputs(s), exp, f"trial {trial}")
+        if trial % 4 == 0:
+            _full_kv_check(rt, w, b, s, exp)
+        b.close()
+
+
+def test_empty_batch_is_all_padding(rt):
+    ric, runner = rt
+    cfg = ric.make_config(max_num_reqs=4, max_model_len=16, block_size=4, max_blocks_per_req=4,
+                          max_num_batched_tokens=8, num_kv_blocks=10, null_block=3, staging_bytes=0)
+    b = runner.Batch(cfg)
+    ric.ric_schedule(b.h, [], [])
+    s = b.compile(8)
+    got = b.step_outputs(s)
+    assert list(got["slot_mapping"]) == [12] * 8 and list(got["req_indices"]) == [-1] * 8
+    assert list(got["query_start_loc"]) == [0] * 5 and list(got["seq_lens"]) == [0] * 4
+    assert list(got["sample_indices"]) == [-1] * 4 and got["num_sampled"] == 0
+    b.close()
+
+
+def test_serving_loop_deltas(rt):
+    """Several steps of a simulated serving loop on one handle: requests
+    arrive, decode (one appended token per step, a new block when the last one
+    fills), get preempted and resume with replaced blocks, finish, get aborted
+    and resubmitted under the same id; the batch is condensed.  Every step's
+    compile equals the oracle's compile of the reference batch."""
+    ric, runner = rt
+    rng = np.random.default_rng(99)
+    B, MR, M = 4, 12, 96
+    cfg = ric.make_config(max_num_reqs=MR, max_model_len=M, block_size=B, max_blocks_per_req=M // B,
+                          max_num_batched_tokens=128, num_kv_blocks=4096, null_block=0, staging_bytes=0)
+    b = runner.Batch(cfg)
+    ref = ref_batch.RefBatch(MR, M, M // B, 4096)
+    free_blocks = list(rng.permutation(np.arange(1, 4096)))
+    state = {}   # req_id -> dict(T, c)
+    next_id = 0
+
+    def new_blocks(n):
+        return [int(free_blocks.pop()) for _ in range(n)]
+
+    for step_no in range(40):
+        # finish / abort-resubmit / preempt some requests
+        for rid in list(state):
+            x = rng.random()
+            if x < 0.12:
+                ric.ric_remove_request(b.h, rid); ref.remove_request(rid); del state[rid]
+            elif x < 0.16:   # abort and resubmit under the same id: a new request
+                ric.ric_remove_request(b.h, rid); ref.remove_request(rid)
+                T = int(rng.integers(1, 30))
+                toks = rng.integers(0, 1000, T)
+                blks = new_blocks(-(-T // B))
+                ric.ric_add_request(b.h, rid, toks, T, 0, blks); ref.add_request(rid, toks, T, 0, blks)
+                state[rid] = dict(T=T, c=0)
+            elif x < 0.20 and state[rid]["c"] > 0:   # preempted and resumed: blocks replaced
+                st = state[rid]
+                blks = new_blocks(min(-(-st["T"] // B) + 1, M // B))
+                ric.ric_replace_blocks(b.h, rid, blks); ref.replace_blocks(rid, blks)
+        # arrivals
+        while len(state) < MR and rng.random() < 0.6:
+            T = int(rng.integers(1, 40))
+            toks = rng.integers(0, 1000, T)
+            c0 = int(rng.integers(0, T))     # prefix-cache hit
+            blks = new_blocks(-(-T // B))
+            ric.ric_add_request(b.h, next_id, toks, T, c0, blks); ref.add_request(next_id, toks, T, c0, blks)
+            state[next_id] = dict(T=T, c=c0)
+            next_id += 1
+        ric.ric_condense(b.h)
+        ref.condense()
+        order = [rid for rid in ref.req_ids_by_row() if rid is not None]
+        assert b.row_order() == order
+        if not order:
+            continue
+        cs, qs = [], []
+        for rid in order:
+            st = state[rid]
+            if st["c"] >= st["T"]:           # decode: one new token appended
+                tok = [int(rng.integers(0, 1000))]
+                ric.ric_append_tokens(b.h, rid, tok); ref.append_tokens(rid, tok)
+                st["T"] += 1
+                nb = len(ref.rows[ref.row_of[rid]].blocks)
+                if nb * B < st["T"]:
+                    blk = new_blocks(1)
+                    ric.ric_append_blocks(b.h, rid, blk); ref.append_blocks(rid, blk)
+            q = min(st["T"] - st["c"], int(rng.integers(1, 9)))
+            cs.append(st["c"]); qs.append(q)
+        ric.ric_schedule(b.h, cs, qs)
+        ref.schedule(cs, qs)
+        rows = ref.step_rows()
+        N = sum(qs)
+        n_pad = N + int(rng.integers(0, 4))
+        want = ref_step.compile_step(rows, block_size=B, max_num_reqs=MR, max_model_len=M,
+                                     max_num_batched_tokens=128, num_kv_blocks=4096, n_pad=n_pad)
+        s = b.compile(n_pad)
+        got = b.step_outputs(s)
+        for k in ("input_ids", "positions", "req_indices", "slot_mapping", "query_start_loc", "seq_lens",
+                  "logits_indices", "discard", "sample_indices"):
+            assert np.array_equal(np.asarray(got[k], np.int64), np.asarray(want[k], np.int64)), \
+                f"step {step_no} {k}"
+        for rid, q in zip(order, qs):
+            state[rid]["c"] += q
+    b.close()
+
+
+def test_error_paths_leave_state_unchanged(rt):
+    ric, runner = rt
+    cfg = ric.make_config(max_num_reqs=2, max_model_len=16, block_size=4, max_blocks_per_req=4,
+                          max_num_batched_tokens=8, num_kv_blocks=10, null_block=0, staging_bytes=0)
+    b = runner.Batch(cfg)
+    h = b.h
+    ric.ric_add_request(h, 1, [5, 6, 7], 3, 0, [2])
+
+    def code(fn, *a):
+        with pytest.raises(ric.RicError) as e:
+            fn(*a)
+        return e.value.code
+
+    assert code(ric.ric_add_request, h, 1, [1], 1, 0, [3]) == ric.RIC_EEXIST
+    assert code(ric.ric_add_request, h, 2, [1] * 17, 1, 0, [3]) == ric.RIC_ERANGE
+    assert code(ric.ric_add_request, h, 2, [1], 1, 0, [0]) == ric.RIC_ERANGE       # null block
+    assert code(ric.ric_add_request, h, 2, [1], 1, 0, [10]) == ric.RIC_ERANGE      # beyond the pool
+    assert code(ric.ric_remove_request, h, 9) == ric.RIC_ENOENT
+    assert code(ric.ric_append_tokens, h, 1, [0] * 14) == ric.RIC_EFULL
+    assert code(ric.ric_append_blocks, h, 1, [1, 2, 3, 4]) == ric.RIC_EFULL
+    assert code(ric.ric_schedule, h, [0], [0]) == ric.RIC_EINVAL                   # q = 0
+    assert code(ric.ric_schedule, h, [1], [3]) == ric.RIC_EINVAL                   # past the history
+    assert code(ric.ric_schedule, h, [0, 0], [1, 1]) == ric.RIC_EINVAL             # R != live
+    assert code(ric.ric_compile, h, 8) == ric.RIC_ESTATE                           # not scheduled
+    ric.ric_add_request(h, 2, [1, 2, 3, 4, 5], 5, 0, [3])
+    assert code(ric.ric_add_request, h, 3, [1], 1, 0, [4]) == ric.RIC_EFULL       # no free row
+    assert code(ric.ric_schedule, h, [0, 0], [3, 5]) == ric.RIC_EINVAL             # too few blocks
+    ric.ric_remove_request(h, 1)
+    assert code(ric.ric_schedule, h, [0], [1]) == ric.RIC_ESTATE                   # hole at row 0
+    assert ric.ric_condense(h) == 1
+    ric.ric_schedule(h, [0], [4])
+    assert code(ric.ric_compile, h, 3) == ric.RIC_EINVAL                           # N_pad < N
+    assert code(ric.ric_compile, h, 9) == ric.RIC_EINVAL                           # above the budget
+    s = b.compile(4)
+    got = b.step_outputs(s)
+    assert list(got["input_ids"]) == [1, 2, 3, 4]
+    assert list(got["slot_mapping"]) == [12, 13, 14, 15]
+    assert ric.ric_num_reqs(h) == 1 and ric.ric_row_of(h, 2) == 0 and ric.ric_req_at(h, 1) is None
+    b.close()
+
+
+def test_out_of_range_indices_are_reported_not_written(rt):
+    """The copy kernels' own bounds checks: a slot outside the cache or an
+    index past the source rows is skipped (zero row for the gather) and counted
+    in the status word; in-range rows are still written."""
+    ric, runner = rt
+    row_bytes = 64
+    nslots = 32
+    k = torch.arange(4 * 32, dtype=torch.int16, device="cuda").reshape(4, 32)
+    v = k + 1000
+    kc = torch.full((nslots, 32), -1, dtype=torch.int16, device="cuda")
+    vc = torch.full((nslots, 32), -1, dtype=torch.int16, device="cuda")
+    slot = torch.tensor([3, nslots, -5, 7], dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ric.ric_reshape_and_cache([k.data_ptr()], [v.data_ptr()], [kc.data_ptr()], [vc.data_ptr()],
+                              slot.data_ptr(), 4, row_bytes, nslots, dev_status=status.data_ptr(),
+                              stream=runner.current_stream())
+    torch.cuda.synchronize()
+    assert int(status.item()) == 4        # two bad tokens, K and V rows each
+    assert torch.equal(kc[3], k[0]) and torch.equal(vc[7], v[3])
+    others = [i for i in range(nslots) if i not in (3, 7)]
+    assert bool((kc[others] == -1).all()) and bool((vc[others] == -1).all())
+    src = torch.arange(5 * 16, dtype=torch.int32, device="cuda").reshape(5, 16)
+    idx = torch.tensor([4, 5, -1, 0], dtype=torch.int32, device="cuda")
+    out = torch.full((4, 16), 9, dtype=torch.int32, device="cuda")
+    status.zero_()
+    ric.ric_gather_rows(src.data_ptr(), 64, 5, idx.data_ptr(), 0, 4, 64, out.data_ptr(), 64,
+                        status.data_ptr(), runner.current_stream())
+    torch.cuda.synchronize()
+    assert int(status.item()) == 1
+    assert torch.equal(out[0], src[4]) and torch.equal(out[3], src[0])
+    assert bool((out[1] == 0).all()) and bool((out[2] == 0).all())
