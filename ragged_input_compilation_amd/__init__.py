@@ -6,15 +6,14 @@ side is a thin ctypes binding (``_ric``) plus a step driver (``runner``) that
 allocates device memory and streams with PyTorch and calls the library.
 Importing ``_ric`` fails loudly when the library has not been built: there is no
 fallback implementation."""
+import importlib
 
 __all__ = ["ric", "runner"]
 
+_LAZY = {"ric": "._ric", "runner": ".runner"}
+
 
 def __getattr__(name):
-    if name == "ric":
-        from . import _ric
-        return _ric
-    if name == "runner":
-        from . import runner
-        return runner
+    if name in _LAZY:
+        return importlib.import_module(_LAZY[name], __name__)
     raise AttributeError(name)
