@@ -1,0 +1,392 @@
+#!/usr/bin/env python3
+"""Benchmark of the ragged-input step on one MI355X.
+
+One step = compile the persistent batch into the flat token stream and its
+metadata (one kernel), write the step's K/V rows into the paged caches of every
+layer (one kernel), gather the hidden rows that produce logits (one kernel).
+Inputs (column store, K/V sources, hidden states) are resident in HBM before
+the timed region.  Steps rotate over independently seeded instances of the
+same configuration (different block tables, token histories and K/V sources),
+so a step never finds the previous steps' bytes in the 256 MB Infinity Cache.
+
+Prints one JSON line.  Extra fields: per-kernel times from HIP events, the
+step's algorithmic bytes and GB/s, the rate including the host-to-device
+upload of the step's counts, and the CPU oracle's rate (single thread)."""
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import mmap
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "scheduled tokens/sec per step (compile + KV write); achieved HBM GB/s vs peak"
+DESCRIPTIONS = {
+    "worked_example": "3 requests (prefill 7, decode 5+1, chunk 10..21), N=20 padded to 32, block 16, "
+                      "f16 K/V 2x64, 1 layer",
+    "decode_heavy": "256 single-token decodes, contexts U[128,4096], block 16, bf16 K/V 8x128, 32 layers",
+    "mixed": "prefills 2000+512, two 2048-token chunk middles, 120 decodes (N=6728), block 16, "
+             "bf16 K/V 8x128, 1 layer",
+    "churn": "1024-row persistent batch after 10% churn + condense + refill, 960 decodes + 64 prefill "
+             "chunks (N=16384), block 16, bf16 K/V 8x128, 1M-block pool, 1 layer",
+    "long_context": "4 requests x 8192-token chunks of 131072-token prompts, cached prefix U[0,122880], "
+                    "block 64, bf16 K/V 8x128, 1 layer, compacted hidden gather",
+    "long_context_forced": "long_context with request 0 at its last chunk (one compacted gather row)",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="long_context", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--sets", type=int, default=0, help="rotation instances (0: enough for >= 1 GiB/cycle)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB copy (identity-index row gather) for counter scaling")
+    return ap.parse_args()
+
+
+def step_bytes(w):
+    """Algorithmic bytes of one step (what the method must read and write;
+    padding, over-fetch and cache-line granularity excluded)."""
+    live = w.live_requests()
+    R = len(live)
+    N = sum(r.num_scheduled for r in live)
+    B = w.block_size
+    touched = sum(-(-(r.num_computed + r.num_scheduled) // B) - r.num_computed // B for r in live)
+    compile_b = 12 * R + 4 * N + 4 * touched + 16 * N + 4 * (R + 1) + 4 * R + 4 * R + 4 * R + R
+    kv_b = w.num_layers * (2 * N * w.row_bytes + 4 * N + 2 * N * w.row_bytes)
+    if w.gather == "all":
+        m = R
+    else:
+        m = sum(1 for r in live if r.num_computed + r.num_scheduled >= r.num_prompt)
+    gather_b = 2 * m * w.hidden_size * 2 + 4 * m
+    return dict(R=R, N=N, compile=compile_b, kv=kv_b, gather=gather_b, gather_rows=m,
+                total=compile_b + kv_b + gather_b)
+
+
+def kernel_source_digest():
+    with open(os.path.join(ROOT, "ragged_input_compilation_amd", "csrc", "ric_kernels.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic(workload_name):
+    """HBM traffic of the K/V kernel from committed counter runs, if they were
+    taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"kv_scatter_{workload_name}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+class GpuStep:
+    """Prebuilt library calls for one rotation instance."""
+
+    def __init__(self, ric, runner, torch, w, kc, vc, hidden, out, seed):
+        self.w = w
+        self.batch = runner.Batch(runner.config_of(w))
+        self.batch.load_history(w)
+        self.batch.schedule_from(w)
+        live = w.live_requests()
+        self.N = sum(r.num_scheduled for r in live)
+        self.n_pad = ric.ric_padded_size(w.capture_sizes, self.N)
+        self.step = ric.ric_compile(self.batch.h, self.n_pad)
+        self.k, self.v = runner.alloc_sources(w, self.n_pad, seed=seed)
+        L = w.num_layers
+        P = ctypes.c_void_p * L
+        self._ptrs = [P(*[t.data_ptr() for t in lst]) for lst in (self.k, self.v, kc, vc)]
+        pp = ctypes.POINTER(ctypes.c_void_p)
+        self.stream = runner.current_stream()
+        st = ctypes.c_void_p(self.stream or None)
+        lib = ric.lib()
+        self.lib = lib
+        self.kv_args = [ctypes.cast(a, pp) for a in self._ptrs] + [
+            L, ctypes.c_void_p(self.step.slot_mapping), self.n_pad, 0, w.row_bytes,
+            w.num_kv_blocks * w.block_size, None, st]
+        row = w.hidden_size * 2
+        if w.gather == "all":
+            idx, cnt, rows = self.step.logits_indices, None, len(live)
+        else:
+            idx, cnt, rows = self.step.sample_indices, self.step.dev_scalars + 20, w.max_num_reqs
+        self.gather_args = [ctypes.c_void_p(hidden.data_ptr()), row, hidden.shape[0], ctypes.c_void_p(idx),
+                            ctypes.c_void_p(cnt), rows, row, ctypes.c_void_p(out.data_ptr()), row, None, st]
+        self.h = ctypes.c_void_p(self.batch.h)
+        self.step_out = ric.ric_step()
+        self.ric = ric
+
+    def _check(self, rc):
+        if rc != 0:
+            raise RuntimeError(self.ric.ric_last_error())
+
+    def compile(self):
+        self._check(self.lib.ric_compile(self.h, self.n_pad, ctypes.byref(self.step_out)))
+
+    def kv(self):
+        self._check(self.lib.ric_reshape_and_cache(*self.kv_args))
+
+    def gather(self):
+        self._check(self.lib.ric_gather_rows(*self.gather_args))
+
+    def reschedule(self):
+        """Host counts -> pinned staging (uploaded by the next compile)."""
+        live_rows = self.batch.row_order()
+        by_id = self.w.by_id()
+        if not hasattr(self, "_sched"):
+            c = [by_id[i].num_computed for i in live_rows]
+            q = [by_id[i].num_scheduled for i in live_rows]
+            self._sched = [self.ric._i32(c), self.ric._i32(q)]
+        (ca, cp), (qa, qp) = self._sched
+        self._check(self.lib.ric_schedule(self.h, ca.shape[0], cp, qp))
+
+
+def cpu_baseline(w, seconds):
+    """The plain C oracle, single thread: compile + K/V scatter into mmap'd host
+    caches of the full size + gather, repeated over the full step."""
+    import numpy as np
+    from oracle import batch as ref_batch, cbind
+    from workloads import payload_numpy
+
+    ref = ref_batch.RefBatch(w.max_num_reqs, w.max_model_len, w.max_blocks_per_req, w.num_kv_blocks)
+    for r in w.initial:
+        ref.add_request(r.req_id, r.tokens, r.num_prompt, r.num_computed, r.blocks)
+    for rid in w.finished:
+        ref.remove_request(rid)
+    ref.condense()
+    for r in w.refill:
+        ref.add_request(r.req_id, r.tokens, r.num_prompt, r.num_computed, r.blocks)
+    by_id = w.by_id()
+    order = [rid for rid in ref.req_ids_by_row() if rid is not None]
+    ref.schedule([by_id[i].num_computed for i in order], [by_id[i].num_scheduled for i in order])
+    rows = ref.step_rows()
+    N = sum(r.num_scheduled for r in rows)
+    n_pad = N
+    for s in sorted(w.capture_sizes):
+        if s >= N:
+            n_pad = s
+            break
+    tok, blk = cbind.pack_tables(rows)
+    lib = cbind.lib()
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    c = np.ascontiguousarray([r.num_computed for r in rows], np.int32)
+    q = np.ascontiguousarray([r.num_scheduled for r in rows], np.int32)
+    P = np.ascontiguousarray([r.num_prompt for r in rows], np.int32)
+    MR = w.max_num_reqs
+    outs = {k: np.zeros(n_pad, np.int32) for k in ("ids", "pos", "req", "slot")}
+    per = {k: np.zeros(MR + 1, np.int32) for k in ("qsl", "cuk", "seq", "log", "smp")}
+    disc = np.zeros(MR, np.uint8)
+    p = lambda a: a.ctypes.data_as(i32p)
+    ins = cbind._In(len(rows), w.block_size, MR, n_pad, 0, tok.shape[1], blk.shape[1], p(c), p(q), p(P),
+                    p(tok), p(blk))
+    out = cbind._Out(p(outs["ids"]), p(outs["pos"]), p(outs["req"]), p(outs["slot"]), p(per["qsl"]),
+                     p(per["cuk"]), p(per["seq"]), p(per["log"]), disc.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
+                     p(per["smp"]), 0, 0, 0, 0)
+    rng = np.random.default_rng(w.seed + 99)
+    L = w.num_layers
+    row = w.row_bytes
+    k_src = [payload_numpy(rng, (n_pad, row // 2), w.kv_dtype) for _ in range(L)]
+    v_src = [payload_numpy(rng, (n_pad, row // 2), w.kv_dtype) for _ in range(L)]
+    nslots = w.num_kv_blocks * w.block_size
+    flags = mmap.MAP_PRIVATE | mmap.MAP_ANONYMOUS | getattr(mmap, "MAP_NORESERVE", 0x4000)
+    maps = [mmap.mmap(-1, nslots * row, flags=flags) for _ in range(2 * L)]
+    caches = [np.frombuffer(m, dtype=np.uint8) for m in maps]
+    hidden = np.zeros((n_pad, w.hidden_size * 2), np.uint8)     # lazily mapped zero pages
+    m_rows = MR
+    gout = np.zeros((m_rows, w.hidden_size * 2), np.uint8)
+
+    def one_step():
+        if lib.nano_compile(ctypes.byref(ins), ctypes.byref(out)) != 0:
+            raise RuntimeError("oracle rejected the step")
+        for l in range(L):
+            lib.nano_kv_scatter(k_src[l].ctypes.data, v_src[l].ctypes.data, caches[2 * l].ctypes.data,
+                                caches[2 * l + 1].ctypes.data, p(outs["slot"]), n_pad, row)
+        idx = per["log"] if w.gather == "all" else per["smp"]
+        cnt = len(rows) if w.gather == "all" else out.num_sampled
+        lib.nano_gather(hidden.ctypes.data, hidden.shape[1], p(idx), cnt, gout.ctypes.data)
+
+    one_step()                     # pre-fault the touched cache pages
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        one_step()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 10000:
+            break
+    del caches
+    for m in maps:
+        m.close()
+    return dict(value=N * reps / el, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"{reps} full steps of the same configuration (seed instance 0) in {el:.1f} s; "
+                       f"single-thread C oracle (nano-vllm block-range compile, memcpy K/V scatter into "
+                       f"mmap'd full-size host caches, hidden-row gather)")
+
+
+def calibrate_copy(ric, torch, stream):
+    """A plain copy of known size through the row-gather kernel with identity
+    indices: 16384 rows of 16 KiB (256 MiB read, 256 MiB written)."""
+    rows, row = 16384, 16384
+    src = torch.empty((rows, row), dtype=torch.uint8, device="cuda").random_(0, 255)
+    dst = torch.empty_like(src)
+    idx = torch.arange(rows, dtype=torch.int32, device="cuda")
+    times = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        ric.ric_gather_rows(src.data_ptr(), row, rows, idx.data_ptr(), 0, rows, row, dst.data_ptr(), row, 0, stream)
+        b.record()
+        times.append((a, b))
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+    ms = sorted(a.elapsed_time(b) for a, b in times)[len(times) // 2]
+    return dict(bytes_read=rows * row, bytes_written=rows * row, ms=ms,
+                gbps=2 * rows * row / (ms * 1e-3) / 1e9, grid=rows)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: this step needs no exchange between GPUs and every box here has "
+              f"one GPU (asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import workloads
+    from ragged_input_compilation_amd import _ric as ric, runner
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    w0 = workloads.get(args.config)
+    sb = step_bytes(w0)
+    S = args.sets or max(2, min(16, math.ceil((1 << 30) / sb["total"])))
+    t_setup = time.perf_counter()
+    kc, vc = runner.alloc_caches(w0)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(w0.seed + 5)
+    n_pad0 = ric.ric_padded_size(w0.capture_sizes, sb["N"])
+    hidden = torch.randn((n_pad0, w0.hidden_size), generator=g, device="cuda").to(torch.bfloat16)
+    gout = torch.empty((w0.max_num_reqs, w0.hidden_size), dtype=torch.bfloat16, device="cuda")
+    sets = []
+    for k in range(S):
+        w = w0 if k == 0 else workloads.get(args.config, variant=k)
+        sets.append(GpuStep(ric, runner, torch, w, kc, vc, hidden, gout, seed=w.seed + 31))
+        print(f"[bench] set {k + 1}/{S} ready", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+
+    def run(n, record):
+        ev = []
+        for i in range(n):
+            st = sets[i % S]
+            if record:
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+                e[0].record()
+                st.compile()
+                e[1].record()
+                st.kv()
+                e[2].record()
+                st.gather()
+                e[3].record()
+                ev.append(e)
+            else:
+                st.compile()
+                st.kv()
+                st.gather()
+        return ev
+
+    run(args.warmup, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev = run(args.steps, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    comp_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    kv_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    ga_ms = [e[2].elapsed_time(e[3]) for e in ev]
+    mean = lambda xs: sum(xs) / len(xs)
+    kv_mean = mean(kv_ms)
+
+    # Same step with the counts uploaded from the host first (schedule + the
+    # flush inside compile carry them over PCIe).
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    n_pcie = max(args.steps // 2, 1)
+    for i in range(n_pcie):
+        st = sets[i % S]
+        st.reschedule()
+        st.compile()
+        st.kv()
+        st.gather()
+    torch.cuda.synchronize()
+    pcie_ms = (time.perf_counter() - t1) * 1e3 / n_pcie
+
+    # A cold-cache check on one step: the MALL and L2 flushed by a 1 GiB write.
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    cold = []
+    for i in range(5):
+        flush_buf.fill_(i)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        sets[i % S].kv()
+        b.record()
+        cold.append((a, b))
+    torch.cuda.synchronize()
+    kv_cold_ms = sorted(a.elapsed_time(b) for a, b in cold)[2]
+    del flush_buf
+
+    calib = calibrate_copy(ric, torch, runner.current_stream()) if args.calibrate_copy else None
+
+    N = sb["N"]
+    achieved = sb["kv"] / (kv_mean * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": N / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int32",
+        "data": "synthetic",
+        "config": {"workload": f"{args.config}: {DESCRIPTIONS[args.config]}", "num_reqs": sb["R"],
+                   "num_tokens": N, "num_layers": w0.num_layers, "rotation_instances": S},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": load_traffic(args.config),
+                     "kernel": "kv_scatter_kernel", "bytes_per_launch": sb["kv"],
+                     "avg_launch_us": kv_mean * 1e3},
+        "step_bytes": sb["total"],
+        "step_gbps": sb["total"] / (ms_per_step * 1e-3) / 1e9,
+        "step_frac_of_peak": sb["total"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "kernels_us": {"compile": mean(comp_ms) * 1e3, "kv_scatter": kv_mean * 1e3,
+                       "gather": mean(ga_ms) * 1e3, "kv_scatter_after_cache_flush": kv_cold_ms * 1e3},
+        "pcie_inclusive_tokens_per_s": N / (pcie_ms * 1e-3),
+        "setup_s": setup_s,
+    }
+    if calib:
+        res["copy_calibration"] = calib
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w0, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

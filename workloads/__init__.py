@@ -95,8 +95,8 @@ class Workload:
         return {r.req_id: r for r in self.initial + self.refill}
 
 
-def _rng(index: int, salt: int = 0) -> np.random.Generator:
-    return np.random.default_rng(SEED_BASE + index + (salt << 8))
+def _rng(index: int, variant: int = 0) -> np.random.Generator:
+    return np.random.default_rng(SEED_BASE + index + (variant << 8))
 
 
 def _sampling(rng: np.random.Generator):
@@ -132,9 +132,9 @@ def _mk(rng, pool, req_id, vocab, block_size, c, q, P, T) -> Req:
     return Req(req_id, tokens, P, c, q, blocks, **_sampling(rng))
 
 
-def worked_example() -> Workload:
+def worked_example(variant: int = 0) -> Workload:
     """Rows A (prefill 7), B (decode, 5 cached + 1 new), C (chunk computing 10..21)."""
-    rng = _rng(0)
+    rng = _rng(0, variant)
     pool = _BlockPool(rng, 32)
     B = 16
     a = _mk(rng, pool, 0, 32000, B, c=0, q=7, P=7, T=7)
@@ -143,12 +143,12 @@ def worked_example() -> Workload:
     return Workload("worked_example", block_size=B, max_num_reqs=4, max_model_len=64,
                     max_blocks_per_req=4, max_num_batched_tokens=32, num_kv_blocks=32,
                     kv_heads=2, head_dim=64, kv_dtype="f16", num_layers=1, hidden_size=128,
-                    gather="all", initial=[a, b, c], seed=SEED_BASE + 0)
+                    gather="all", initial=[a, b, c], seed=SEED_BASE + 0 + (variant << 8))
 
 
-def decode_heavy() -> Workload:
+def decode_heavy(variant: int = 0) -> Workload:
     """256 decodes, cached context U[128,4096], prompt U[1,c]; 32 layers of K/V."""
-    rng = _rng(1)
+    rng = _rng(1, variant)
     pool = _BlockPool(rng, 131072)
     B = 16
     reqs = []
@@ -159,14 +159,14 @@ def decode_heavy() -> Workload:
     return Workload("decode_heavy", block_size=B, max_num_reqs=512, max_model_len=8192,
                     max_blocks_per_req=512, max_num_batched_tokens=256, num_kv_blocks=131072,
                     kv_heads=8, head_dim=128, kv_dtype="bf16", num_layers=32, hidden_size=4096,
-                    gather="all", initial=reqs, seed=SEED_BASE + 1)
+                    gather="all", initial=reqs, seed=SEED_BASE + 1 + (variant << 8))
 
 
-def mixed() -> Workload:
+def mixed(variant: int = 0) -> Workload:
     """Prefills of 2000 and 512, two 2048-token chunk middles over 2048 cached
     tokens of 8192-token prompts, and 120 decodes with contexts U[256,8192];
     rows in a seeded order."""
-    rng = _rng(2)
+    rng = _rng(2, variant)
     pool = _BlockPool(rng, 65536)
     B = 16
     shapes = [(0, 2000, 2000, 2000), (0, 512, 512, 512),
@@ -179,15 +179,15 @@ def mixed() -> Workload:
     return Workload("mixed", block_size=B, max_num_reqs=128, max_model_len=16384,
                     max_blocks_per_req=1024, max_num_batched_tokens=8704, num_kv_blocks=65536,
                     kv_heads=8, head_dim=128, kv_dtype="bf16", num_layers=1, hidden_size=4096,
-                    gather="all", initial=reqs, seed=SEED_BASE + 2)
+                    gather="all", initial=reqs, seed=SEED_BASE + 2 + (variant << 8))
 
 
-def churn() -> Workload:
+def churn(variant: int = 0) -> Workload:
     """1024 live rows; a seeded 102 finish; the batch is condensed and 102 new
     requests fill the tail.  The 1024 rows then alive get seeded roles: 960
     decodes and 64 prefill chunks whose sizes are a seeded composition of 15424
     (token budget 16384)."""
-    rng = _rng(3)
+    rng = _rng(3, variant)
     pool = _BlockPool(rng, 1 << 20)
     B, M = 16, 32768
     n_init, n_fin = 1024, 102
@@ -214,15 +214,15 @@ def churn() -> Workload:
                     max_blocks_per_req=M // B, max_num_batched_tokens=16384,
                     num_kv_blocks=1 << 20, kv_heads=8, head_dim=128, kv_dtype="bf16",
                     num_layers=1, hidden_size=4096, gather="all", initial=initial,
-                    finished=finished, refill=refill, seed=SEED_BASE + 3)
+                    finished=finished, refill=refill, seed=SEED_BASE + 3 + (variant << 8))
 
 
-def long_context(force_complete: bool = False) -> Workload:
+def long_context(force_complete: bool = False, variant: int = 0) -> Workload:
     """4 requests with 131072-token prompts, each computing an 8192-token chunk
     on a seeded cached prefix U[0,122880]; block size 64.  With
     ``force_complete`` request 0 sits at the last chunk (cached 122880), so the
     compacted hidden-state gather has at least one row."""
-    rng = _rng(4)
+    rng = _rng(4, variant)
     pool = _BlockPool(rng, 16384)
     B, M = 64, 131072
     reqs = []
@@ -235,16 +235,18 @@ def long_context(force_complete: bool = False) -> Workload:
                     max_num_reqs=4, max_model_len=M, max_blocks_per_req=M // B,
                     max_num_batched_tokens=32768, num_kv_blocks=16384, kv_heads=8,
                     head_dim=128, kv_dtype="bf16", num_layers=1, hidden_size=8192,
-                    gather="compacted", initial=reqs, seed=SEED_BASE + 4)
+                    gather="compacted", initial=reqs, seed=SEED_BASE + 4 + (variant << 8))
 
 
 _BUILDERS = {"worked_example": worked_example, "decode_heavy": decode_heavy,
              "mixed": mixed, "churn": churn, "long_context": long_context,
-             "long_context_forced": lambda: long_context(True)}
+             "long_context_forced": lambda variant=0: long_context(True, variant)}
 
 
-def get(name: str) -> Workload:
-    return _BUILDERS[name]()
+def get(name: str, variant: int = 0) -> Workload:
+    """The named configuration; ``variant`` > 0 draws an independent instance
+    of the same configuration (same shapes and distributions, other seed)."""
+    return _BUILDERS[name](variant=variant)
 
 
 def random_batch(rng: np.random.Generator, *, num_reqs: int, block_size: int,
