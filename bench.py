@@ -26,6 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+KV_EVENT_EVERY = 4      # timed steps carrying events around the K/V launch: 1 in 4
 METRIC = "scheduled tokens/sec per step (compile + KV write); achieved HBM GB/s vs peak"
 DESCRIPTIONS = {
     "worked_example": "3 requests (prefill 7, decode 5+1, chunk 10..21), N=20 padded to 32, block 16, "
@@ -74,22 +75,34 @@ def step_bytes(w):
                 total=compile_b + kv_b + gather_b)
 
 
+def kv_kernel_name(w, n_tokens):
+    """Which K/V launch shape the library picks for this size (mirrors its
+    launcher: wave rows for <= 2048 tokens of 1/2/4 KiB rows, else chunk tiles)."""
+    cpl = w.row_bytes // 1024
+    if w.row_bytes % 1024 == 0 and cpl in (1, 2, 4) and n_tokens <= 2048:
+        return "kv_wave_kernel"
+    return "kv_chunk_kernel"
+
+
 def kernel_source_digest():
     with open(os.path.join(ROOT, "ragged_input_compilation_amd", "csrc", "ric_kernels.hip"), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def load_traffic(workload_name):
-    """HBM traffic of the K/V kernel from committed counter runs, if they were
-    taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"kv_scatter_{workload_name}_pmc.json")
+def load_traffic(kernel_name, workload_name):
+    """HBM bytes per launch of the K/V kernel from the committed counter runs
+    (profiles/<kernel>_<workload>_pmc.md), or None when there are none or they
+    were taken on another version of the kernel source."""
+    import re
+    path = os.path.join(ROOT, "profiles", f"{kernel_name}_{workload_name}_pmc.md")
     if not os.path.exists(path):
         return None
-    with open(path) as f:
-        d = json.load(f)
-    if d.get("kernel_source_sha256") != kernel_source_digest():
+    text = open(path, encoding="utf-8").read()
+    digest = re.search(r"^kernel_source_sha256: ([0-9a-f]{64})$", text, re.M)
+    traffic = re.search(r"^traffic_bytes_per_launch: (\d+)$", text, re.M)
+    if not digest or not traffic or digest.group(1) != kernel_source_digest():
         return None
-    return d.get("traffic_bytes_per_launch")
+    return int(traffic.group(1))
 
 
 class GpuStep:
@@ -287,38 +300,57 @@ def main():
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 
-    def run(n, record):
+    def run(n, mode):
+        """mode "none": no events; "kv": events around the K/V launch only (the
+        timed region); "all": events around each of the three kernels."""
         ev = []
         for i in range(n):
             st = sets[i % S]
-            if record:
-                e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-                e[0].record()
+            if mode == "none":
                 st.compile()
-                e[1].record()
                 st.kv()
-                e[2].record()
                 st.gather()
-                e[3].record()
-                ev.append(e)
+            elif mode == "kv" and i % KV_EVENT_EVERY != 0:
+                st.compile()
+                st.kv()
+                st.gather()
+            elif mode == "kv":
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                st.compile()
+                a.record()
+                st.kv()
+                b.record()
+                st.gather()
+                ev.append((a, b))
             else:
-                st.compile()
-                st.kv()
-                st.gather()
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+                e[0].record(); st.compile(); e[1].record()
+                e[2].record(); st.kv(); e[3].record()
+                e[4].record(); st.gather(); e[5].record()
+                ev.append(e)
         return ev
 
-    run(args.warmup, False)
+    run(args.warmup, "none")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev = run(args.steps, True)
+    ev = run(args.steps, "kv")
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    comp_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    kv_ms = [e[1].elapsed_time(e[2]) for e in ev]
-    ga_ms = [e[2].elapsed_time(e[3]) for e in ev]
     mean = lambda xs: sum(xs) / len(xs)
-    kv_mean = mean(kv_ms)
+    kv_mean = mean([a.elapsed_time(b) for a, b in ev])
+
+    # Untimed diagnostics: the same steps with no events, then with events
+    # around every kernel (compile and gather durations).
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    run(args.steps, "none")
+    torch.cuda.synchronize()
+    ms_no_events = (time.perf_counter() - t2) * 1e3 / args.steps
+    evs = run(min(args.steps, 100), "all")
+    torch.cuda.synchronize()
+    comp_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    ga_ms = [e[4].elapsed_time(e[5]) for e in evs]
 
     # Same step with the counts uploaded from the host first (schedule + the
     # flush inside compile carry them over PCIe).
@@ -334,11 +366,12 @@ def main():
     torch.cuda.synchronize()
     pcie_ms = (time.perf_counter() - t1) * 1e3 / n_pcie
 
-    # A cold-cache check on one step: the MALL and L2 flushed by a 1 GiB write.
-    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    # A cold-cache check: before each of 5 K/V launches, a 1 GiB read (a sum)
+    # evicts the Infinity Cache and the L2s without leaving dirty lines behind.
+    flush_buf = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
     cold = []
     for i in range(5):
-        flush_buf.fill_(i)
+        flush_buf.sum()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         sets[i % S].kv()
@@ -368,12 +401,13 @@ def main():
         "config": {"workload": f"{args.config}: {DESCRIPTIONS[args.config]}", "num_reqs": sb["R"],
                    "num_tokens": N, "num_layers": w0.num_layers, "rotation_instances": S},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": load_traffic(args.config),
-                     "kernel": "kv_scatter_kernel", "bytes_per_launch": sb["kv"],
-                     "avg_launch_us": kv_mean * 1e3},
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": load_traffic(kv_kernel_name(w0, sb["N"]), args.config),
+                     "kernel": kv_kernel_name(w0, sb["N"]), "bytes_per_launch": sb["kv"],
+                     "avg_launch_us": kv_mean * 1e3, "event_samples": len(ev)},
         "step_bytes": sb["total"],
         "step_gbps": sb["total"] / (ms_per_step * 1e-3) / 1e9,
         "step_frac_of_peak": sb["total"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "ms_per_step_without_events": ms_no_events,
         "kernels_us": {"compile": mean(comp_ms) * 1e3, "kv_scatter": kv_mean * 1e3,
                        "gather": mean(ga_ms) * 1e3, "kv_scatter_after_cache_flush": kv_cold_ms * 1e3},
         "pcie_inclusive_tokens_per_s": N / (pcie_ms * 1e-3),

@@ -216,13 +216,34 @@ hipError_t launch_compile(const CompileParams& p, hipStream_t s) {
 
 // ---------------------------------------------------------------------------
 // Paged K/V write: row t of every K and V source goes to cache row slot[t]
-// ([P1 §3. 物理 KV 槽位]; [P3 §实现]).  blockIdx.y = 2*layer + (K:0, V:1);
-// blockIdx.x = a run of rows_per_wg token rows.  Lanes walk the run's 16-byte
-// chunks in order, so both the read of a source row and the write of a cache
-// row are contiguous; U chunks per lane are loaded before any is stored.
+// ([P1 §3. 物理 KV 槽位]; [P3 §实现]).  Two launch shapes, chosen by size from
+// a measured sweep on MI355X (the design doc lists the numbers):
+//
+// * chunk tiles (large launches): blockIdx.y = 2*layer + (K:0, V:1),
+//   blockIdx.x = a run of rows of about 4 KiB; lanes walk the run's 16-byte
+//   chunks in order, so a source run is read contiguously and each cache row
+//   is written contiguously.  Plain loads, non-temporal stores.
+// * wave rows (few tokens, many layers): blockIdx.y = layer; each wave owns
+//   ROWS consecutive tokens and copies both the K and the V row of each, so
+//   one wave-uniform (scalar) slot load serves both; 4*ROWS*CPL 16-byte loads
+//   per lane are in flight before any store.  Non-temporal loads, plain
+//   stores.
+//
+// A slot outside [0, num_slots) skips that row and counts it in *status.
 // ---------------------------------------------------------------------------
-template <int U>
-__global__ __launch_bounds__(256) void kv_scatter_kernel(KVParams p) {
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const uint8_t* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    else return *reinterpret_cast<const u32x4*>(p);
+}
+template <bool NT>
+__device__ __forceinline__ void store16(uint8_t* p, u32x4 v) {
+    if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+    else *reinterpret_cast<u32x4*>(p) = v;
+}
+
+template <int U, bool NTL, bool NTS>
+__global__ __launch_bounds__(256) void kv_chunk_kernel(KVParams p) {
     const int tensor = blockIdx.y;
     const int layer = tensor >> 1;
     const bool is_v = (tensor & 1) != 0;
@@ -244,8 +265,7 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(KVParams p) {
                 const int j = i - r * C;
                 const int t = t0 + r;
                 const int s = p.slot[t];
-                val[u] = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x4*>(src + (int64_t)t * p.src_stride + ((int64_t)j << 4)));
+                val[u] = load16<NTL>(src + (int64_t)t * p.src_stride + ((int64_t)j << 4));
                 if (s >= 0 && (int64_t)s < p.num_slots)
                     doff[u] = (int64_t)s * p.row_bytes + ((int64_t)j << 4);
                 else if (j == 0 && p.status != nullptr)
@@ -254,20 +274,79 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(KVParams p) {
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            if (doff[u] >= 0) __builtin_nontemporal_store(val[u], reinterpret_cast<u32x4*>(dst + doff[u]));
+            if (doff[u] >= 0) store16<NTS>(dst + doff[u], val[u]);
     }
 }
 
-constexpr int kKvUnroll = 4;
-constexpr int kKvChunksPerWg = 256 * kKvUnroll;   // 16 KiB per workgroup
+// CPL: 16-byte chunks per lane per row (row_bytes = 1024 * CPL).
+template <int CPL, int ROWS, int WAVES, bool NTL, bool NTS>
+__global__ __launch_bounds__(64 * WAVES) void kv_wave_kernel(KVParams p) {
+    const int layer = blockIdx.y;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int t0 = (blockIdx.x * WAVES + wid) * ROWS;
+    const uint8_t* __restrict__ ks = p.k[layer];
+    const uint8_t* __restrict__ vs = p.v[layer];
+    uint8_t* __restrict__ kd = p.kc[layer];
+    uint8_t* __restrict__ vd = p.vc[layer];
+    u32x4 a[ROWS][2 * CPL];
+    int64_t off[ROWS];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+        const int t = t0 + r;
+        off[r] = -1;
+        if (t < p.num_tokens) {
+            const int s = p.slot[t];
+            const int64_t so = (int64_t)t * p.src_stride + lane * 16;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                a[r][c] = load16<NTL>(ks + so + c * 1024);
+                a[r][CPL + c] = load16<NTL>(vs + so + c * 1024);
+            }
+            if (s >= 0 && (int64_t)s < p.num_slots)
+                off[r] = (int64_t)s * p.row_bytes + lane * 16;
+            else if (lane == 0 && p.status != nullptr)
+                atomicAdd(p.status, 2);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+        if (off[r] >= 0) {
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                store16<NTS>(kd + off[r] + c * 1024, a[r][c]);
+                store16<NTS>(vd + off[r] + c * 1024, a[r][CPL + c]);
+            }
+        }
+    }
+}
+
+constexpr int kKvTileBytes = 4096;        // chunk tiles: about 4 KiB per workgroup
+constexpr int kKvWaveMaxTokens = 2048;    // wave rows up to this many tokens per launch
+constexpr int kKvWaveRows = 4;
+constexpr int kKvWaveWaves = 4;
+
+template <int CPL>
+static void launch_wave(const KVParams& p, int num_layers, hipStream_t s) {
+    const int per_wg = kKvWaveRows * kKvWaveWaves;
+    hipLaunchKernelGGL((kv_wave_kernel<CPL, kKvWaveRows, kKvWaveWaves, true, false>),
+                       dim3((p.num_tokens + per_wg - 1) / per_wg, num_layers), dim3(64 * kKvWaveWaves), 0, s, p);
+}
 
 hipError_t launch_kv_scatter(const KVParams& p_in, int num_layers, hipStream_t s) {
     KVParams p = p_in;
-    const int C = p.row_bytes >> 4;
-    p.rows_per_wg = p.rows_per_wg > 0 ? p.rows_per_wg : (kKvChunksPerWg / C > 0 ? kKvChunksPerWg / C : 1);
+    if (p.num_tokens == 0 || num_layers == 0) return hipSuccess;
+    const int cpl = p.row_bytes / 1024;
+    const bool wave_ok = p.row_bytes % 1024 == 0 && (cpl == 1 || cpl == 2 || cpl == 4);
+    if (wave_ok && p.num_tokens <= kKvWaveMaxTokens) {
+        if (cpl == 1) launch_wave<1>(p, num_layers, s);
+        else if (cpl == 2) launch_wave<2>(p, num_layers, s);
+        else launch_wave<4>(p, num_layers, s);
+        return hipGetLastError();
+    }
+    p.rows_per_wg = p.rows_per_wg > 0 ? p.rows_per_wg : max(1, kKvTileBytes / p.row_bytes);
     const int gx = (p.num_tokens + p.rows_per_wg - 1) / p.rows_per_wg;
-    if (gx == 0) return hipSuccess;
-    hipLaunchKernelGGL(kv_scatter_kernel<kKvUnroll>, dim3(gx, 2 * num_layers), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((kv_chunk_kernel<1, false, true>), dim3(gx, 2 * num_layers), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

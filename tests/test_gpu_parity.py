@@ -391,6 +391,19 @@ def test_out_of_range_indices_are_reported_not_written(rt):
     assert torch.equal(kc[3], k[0]) and torch.equal(vc[7], v[3])
     others = [i for i in range(nslots) if i not in (3, 7)]
     assert bool((kc[others] == -1).all()) and bool((vc[others] == -1).all())
+    # the same on the few-token launch shape (1 KiB rows, wave-per-row kernel)
+    k1 = torch.arange(4 * 512, dtype=torch.int16, device="cuda").reshape(4, 512)
+    v1 = k1 + 7
+    kc1 = torch.full((nslots, 512), -1, dtype=torch.int16, device="cuda")
+    vc1 = torch.full((nslots, 512), -1, dtype=torch.int16, device="cuda")
+    status.zero_()
+    ric.ric_reshape_and_cache([k1.data_ptr()], [v1.data_ptr()], [kc1.data_ptr()], [vc1.data_ptr()],
+                              slot.data_ptr(), 4, 1024, nslots, dev_status=status.data_ptr(),
+                              stream=runner.current_stream())
+    torch.cuda.synchronize()
+    assert int(status.item()) == 4
+    assert torch.equal(kc1[3], k1[0]) and torch.equal(vc1[7], v1[3])
+    assert bool((kc1[others] == -1).all()) and bool((vc1[others] == -1).all())
     src = torch.arange(5 * 16, dtype=torch.int32, device="cuda").reshape(5, 16)
     idx = torch.tensor([4, 5, -1, 0], dtype=torch.int32, device="cuda")
     out = torch.full((4, 16), 9, dtype=torch.int32, device="cuda")
