@@ -58,7 +58,8 @@ typedef struct {
     int32_t max_num_batched_tokens;  /* capacity of the per-token outputs (padded count)  */
     int32_t num_kv_blocks;           /* physical blocks in the cache; num_kv_blocks*B < 2^31 */
     int32_t null_block;              /* reserved block for padded tokens (usually 0)      */
-    int32_t staging_bytes;           /* pinned delta-staging capacity; 0 = default (4 MiB) */
+    int32_t staging_bytes;           /* pinned delta-staging capacity; 0 = default (4 MiB, more
+                                        for large batches); at least 72*max_num_reqs + 64 KiB */
 } ric_config;
 
 /* Per-request sampling values.  They live in the column store and move with
@@ -195,6 +196,10 @@ int ric_get_columns(const ric_batch* b, ric_columns* out);
 
 /* Wait until the handle's stream is idle (tests, teardown; not a step call). */
 int ric_sync(ric_batch* b);
+
+/* Inspection (tests, debugging; not a step call): wait for the device, then
+ * copy `bytes` from a DEVICE address to HOST memory.  Errors: EINVAL, EHIP. */
+int ric_read_device(void* host_dst, const void* dev_src, size_t bytes);
 
 /* ---- step ---------------------------------------------------------------- */
 

@@ -82,6 +82,7 @@ def _load():
         "ric_req_at": (ctypes.c_int, [_vp, ctypes.c_int32, ctypes.POINTER(ctypes.c_uint64)]),
         "ric_get_columns": (ctypes.c_int, [_vp, ctypes.POINTER(ric_columns)]),
         "ric_sync": (ctypes.c_int, [_vp]),
+        "ric_read_device": (ctypes.c_int, [_vp, _vp, ctypes.c_size_t]),
         "ric_schedule": (ctypes.c_int, [_vp, ctypes.c_int32, _i32p, _i32p]),
         "ric_compile": (ctypes.c_int, [_vp, ctypes.c_int32, ctypes.POINTER(ric_step)]),
         "ric_reshape_and_cache": (ctypes.c_int, [ctypes.POINTER(_vp)] * 4 + [
@@ -226,6 +227,13 @@ def ric_get_columns(h: int) -> ric_columns:
 
 def ric_sync(h: int) -> None:
     _err(_lib.ric_sync(_vp(h)))
+
+
+def ric_read_device(dev_src: int, nbytes: int, dtype=np.uint8) -> np.ndarray:
+    """Synchronous copy of device bytes to a new host array (inspection)."""
+    out = np.zeros(nbytes, np.uint8)
+    _err(_lib.ric_read_device(out.ctypes.data_as(_vp), _vp(dev_src), nbytes))
+    return out.view(dtype)
 
 
 # ---- step -------------------------------------------------------------------

@@ -75,6 +75,12 @@ size_t default_staging(const ric_config& c) {
     return std::max<size_t>(4u << 20, 4 * scal_reserve);
 }
 
+// Smallest staging that always makes progress: room for a full scalar-column
+// refresh (reserved by every flush) plus 64 KiB of payload and ops.
+size_t min_staging(const ric_config& c) {
+    return 2 * (size_t)kNumScalarCols * (size_t)c.max_num_reqs * 4 + (64u << 10);
+}
+
 Layout layout_of(const ric_config& c) {
     Layout L{};
     L.tok_stride = round4(c.max_model_len);
@@ -118,8 +124,9 @@ int check_config(const ric_config* c) {
     if ((int64_t)c->num_kv_blocks * c->block_size >= (int64_t(1) << 31))
         return fail(RIC_EINVAL, "num_kv_blocks * block_size must stay below 2^31 (int32 slots)");
     if (c->staging_bytes < 0) return fail(RIC_EINVAL, "staging_bytes negative");
-    if (c->staging_bytes > 0 && (size_t)c->staging_bytes < default_staging(*c) / 4 + 4096)
-        return fail(RIC_EINVAL, "staging_bytes too small for the scalar columns");
+    if (c->staging_bytes > 0 && (size_t)c->staging_bytes < min_staging(*c))
+        return fail(RIC_EINVAL, "staging_bytes %d below the minimum %zu (twice the scalar columns + 64 KiB)",
+                    c->staging_bytes, min_staging(*c));
     return RIC_OK;
 }
 
@@ -649,6 +656,14 @@ int ric_get_columns(const ric_batch* b, ric_columns* o) {
 int ric_sync(ric_batch* b) {
     if (!b) return fail(RIC_EINVAL, "handle is NULL");
     HIP_TRY(hipStreamSynchronize(b->stream));
+    return RIC_OK;
+}
+
+int ric_read_device(void* host_dst, const void* dev_src, size_t bytes) {
+    if (bytes == 0) return RIC_OK;
+    if (!host_dst || !dev_src) return fail(RIC_EINVAL, "NULL pointer argument");
+    HIP_TRY(hipDeviceSynchronize());
+    HIP_TRY(hipMemcpy(host_dst, dev_src, bytes, hipMemcpyDeviceToHost));
     return RIC_OK;
 }
 

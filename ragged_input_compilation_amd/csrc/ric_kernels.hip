@@ -100,22 +100,36 @@ __global__ __launch_bounds__(kCompileThreads) void compile_kernel(CompileParams 
     const int32_t* col_q = p.scal + (int64_t)kNumScheduled * p.max_num_reqs;
     const int32_t* col_P = p.scal + (int64_t)kNumPrompt * p.max_num_reqs;
 
-    // Scan of q: each thread owns a contiguous run of requests.
+    // Each thread owns a contiguous run of at most 32 requests (R <= 8000).
+    // One pass loads q and c (and, in the per-request workgroup, the prompt
+    // length) together, so the counters cost a single dependent round trip.
+    const bool req_wg = (int)blockIdx.x >= p.num_token_tiles;
     const int per = (R + kCompileThreads - 1) / kCompileThreads;
     const int r0 = min(R, tid * per);
     const int r1 = min(R, r0 + per);
-    int local = 0;
+    int local = 0, kept = 0, max_q = 0, max_seq = 0;
+    uint32_t partial = 0;   // bit k: request r0 + k has not reached the end of its prompt
     for (int i = r0; i < r1; ++i) {
         const int q = col_q[i];
+        const int c = col_c[i];
         s_qsl[i] = q;
+        s_base[i] = c;
         local += q;
+        if (req_wg) {
+            const int seq = c + q;
+            const bool part = seq < col_P[i];
+            partial |= (part ? 1u : 0u) << (i - r0);
+            kept += part ? 0 : 1;
+            max_q = max(max_q, q);
+            max_seq = max(max_seq, seq);
+        }
     }
     int N = 0;
     int run = block_exclusive_scan<kCompileThreads>(local, s_tmp, &N);
     for (int i = r0; i < r1; ++i) {
         const int q = s_qsl[i];
         s_qsl[i] = run;
-        s_base[i] = col_c[i] - run;
+        s_base[i] -= run;
         run += q;
     }
     if (tid == 0) s_qsl[R] = N;
@@ -168,23 +182,15 @@ __global__ __launch_bounds__(kCompileThreads) void compile_kernel(CompileParams 
 
     // Per-request outputs (one workgroup).
     const int MR = p.max_num_reqs;
-    int max_q = 0, max_seq = 0, kept = 0;
-    for (int i = r0; i < r1; ++i) {
-        const int q = s_qsl[i + 1] - s_qsl[i];
-        const int seq = s_base[i] + s_qsl[i] + q;   // c_i + q_i
-        max_q = max(max_q, q);
-        max_seq = max(max_seq, seq);
-        kept += (seq >= col_P[i]) ? 1 : 0;
-    }
     int num_sampled = 0;
     int slot_out = block_exclusive_scan<kCompileThreads>(kept, s_tmp, &num_sampled);
     max_q = block_max<kCompileThreads>(max_q, s_tmp);
     max_seq = block_max<kCompileThreads>(max_seq, s_tmp);
     for (int i = r0; i < r1; ++i) {
-        const int seq = s_base[i] + s_qsl[i + 1];
-        const int li = s_qsl[i + 1] - 1;
-        const bool part = seq < col_P[i];
-        p.seq_lens[i] = seq;
+        const int end = s_qsl[i + 1];
+        const int li = end - 1;
+        const bool part = ((partial >> (i - r0)) & 1u) != 0;
+        p.seq_lens[i] = s_base[i] + end;   // c_i + q_i
         p.logits_indices[i] = li;
         p.discard[i] = part ? 1 : 0;
         if (!part) p.sample_indices[slot_out++] = li;
@@ -372,7 +378,16 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherParams p) {
         return;
     }
     const u32x4* in = reinterpret_cast<const u32x4*>(p.src + id * p.src_stride);
-    for (int j = threadIdx.x; j < C; j += 256) out[j] = __builtin_nontemporal_load(in + j);
+    constexpr int U = 4;   // loads in flight per lane before the stores
+    for (int base = threadIdx.x; base < C; base += 256 * U) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (base + u * 256 < C) v[u] = __builtin_nontemporal_load(in + base + u * 256);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (base + u * 256 < C) out[base + u * 256] = v[u];
+    }
 }
 
 hipError_t launch_gather(const GatherParams& p, hipStream_t s) {

@@ -414,3 +414,146 @@ def test_out_of_range_indices_are_reported_not_written(rt):
     assert int(status.item()) == 1
     assert torch.equal(out[0], src[4]) and torch.equal(out[3], src[0])
     assert bool((out[1] == 0).all()) and bool((out[2] == 0).all())
+
+
+def _simple_rows_workload(reqs, B, max_num_reqs, max_model_len, num_kv_blocks, row_heads=8, head_dim=128,
+                          layers=1, name="custom", staging=0):
+    N = sum(r.num_scheduled for r in reqs)
+    return workloads.Workload(name, block_size=B, max_num_reqs=max_num_reqs, max_model_len=max_model_len,
+                              max_blocks_per_req=-(-max_model_len // B), max_num_batched_tokens=N,
+                              num_kv_blocks=num_kv_blocks, kv_heads=row_heads, head_dim=head_dim,
+                              kv_dtype="bf16", num_layers=layers, hidden_size=256, gather="all",
+                              initial=reqs, capture_sizes=[N], seed=4242)
+
+
+def test_library_allocated_workspace_and_stream_switch(rt):
+    """ric_create without a caller workspace (the library allocates), then a
+    switch to another stream; the compile still equals the oracle."""
+    ric, runner = rt
+    w = workloads.get("mixed")
+    ref, order = replay_history(w)
+    exp = expected_step(w, ref)
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        h = ric.ric_create(runner.config_of(w), runner.current_stream())
+        for r in w.initial:
+            ric.ric_add_request(h, r.req_id, r.tokens, r.num_prompt, r.num_computed, r.blocks)
+        other = torch.cuda.Stream()
+        ric.ric_set_stream(h, int(other.cuda_stream))
+        by_id = w.by_id()
+        ric.ric_schedule(h, [by_id[i].num_computed for i in order], [by_id[i].num_scheduled for i in order])
+        s = ric.ric_compile(h, exp["n_pad"])
+        ric.ric_sync(h)
+        got = {k: _copy_out(getattr(s, k), n)
+               for k, n in (("input_ids", exp["n_pad"]), ("slot_mapping", exp["n_pad"]),
+                            ("positions", exp["n_pad"]), ("query_start_loc", w.max_num_reqs + 1))}
+        ric.ric_destroy(h)
+    for k in got:
+        assert np.array_equal(got[k].astype(np.int64), exp[k]), k
+
+
+def _copy_out(ptr, n):
+    """Read n int32 values at a device address the caller does not own as a tensor."""
+    from ragged_input_compilation_amd import _ric
+    return _ric.ric_read_device(ptr, 4 * n, np.int32)
+
+
+def test_minimum_staging_forces_chunked_uploads(rt):
+    """A staging buffer at its minimum size and a 300k-token request: the
+    payload crosses many flushes; the compiled chunk near the end still reads
+    the right token ids and block entries."""
+    ric, runner = rt
+    rng = np.random.default_rng(11)
+    B, M = 16, 1 << 19
+    T = 300_000
+    c0, q = T - 4096, 4096
+    tokens = rng.integers(0, 1 << 20, size=T).astype(np.int32)
+    blocks = (rng.permutation(40000)[: -(-T // B)] + 1).astype(np.int32)
+    req = workloads.Req(0, tokens, T, c0, q, blocks)
+    w = _simple_rows_workload([req], B, 2, M, 40001)
+    cfg = runner.config_of(w)
+    cfg.staging_bytes = 2 * 9 * 2 * 4 + (64 << 10)
+    b = runner.Batch(cfg)
+    b.load_history(w)
+    ref, order = replay_history(w)
+    b.schedule_from(w, order)
+    exp = expected_step(w, ref)
+    s = b.compile(exp["n_pad"])
+    assert_step_equal(b.step_outputs(s), exp, "min staging")
+    cols = ric.ric_get_columns(b.h)
+    whole = read_rows_i32(b.workspace, cols.tokens, cols.token_stride, [0], T)[0]
+    assert np.array_equal(whole, tokens)
+    b.close()
+    bad = runner.config_of(w)
+    bad.staging_bytes = 1024
+    with pytest.raises(ric.RicError):
+        runner.Batch(bad)
+
+
+def test_more_layers_than_one_launch_holds(rt):
+    """40 layers: the library splits them over launches of at most 32; every
+    layer's cache gets its rows."""
+    ric, runner = rt
+    rng = np.random.default_rng(12)
+    reqs = workloads.random_batch(rng, num_reqs=6, block_size=16, max_model_len=512, num_kv_blocks=256,
+                                  max_q=64, max_c=300)
+    w = _simple_rows_workload(reqs, 16, 8, 512, 256, row_heads=2, head_dim=64, layers=40)
+    b, s, ref, order, exp, _ = _compile(rt, w)
+    _full_kv_check(rt, w, b, s, exp)
+    b.close()
+
+
+def test_max_rows_batch(rt):
+    """8000 rows (the row limit): every thread of the compile owns 32
+    requests; decodes and short prefills mixed."""
+    ric, runner = rt
+    rng = np.random.default_rng(13)
+    reqs = workloads.random_batch(rng, num_reqs=8000, block_size=16, max_model_len=64,
+                                  num_kv_blocks=8000 * 4 + 1, max_q=3, max_c=40)
+    w = _simple_rows_workload(reqs, 16, 8000, 64, 8000 * 4 + 1)
+    b, s, ref, order, exp, _ = _compile(rt, w)
+    assert_step_equal(b.step_outputs(s), exp, "8000 rows")
+    b.close()
+
+
+def test_non_power_of_two_block_size_at_scale(rt):
+    """Block size 48 (a division, not a shift) over long chunks."""
+    ric, runner = rt
+    rng = np.random.default_rng(14)
+    reqs = []
+    pool = rng.permutation(np.arange(1, 5000)).astype(np.int32)
+    nxt = 0
+    for i, (c, q) in enumerate([(1000, 3000), (0, 2500), (4095, 1), (77, 1234)]):
+        T = c + q + int(rng.integers(0, 50))
+        nb = -(-(c + q) // 48)
+        reqs.append(workloads.Req(i, rng.integers(0, 1 << 20, size=T).astype(np.int32), T, c, q,
+                                  pool[nxt:nxt + nb]))
+        nxt += nb
+    w = _simple_rows_workload(reqs, 48, 4, 8192, 5000)
+    b, s, ref, order, exp, _ = _compile(rt, w)
+    assert_step_equal(b.step_outputs(s), exp, "B=48")
+    b.close()
+
+
+def test_strided_sources_from_a_fused_qkv_tensor(rt):
+    """K and V passed as strided views of one [N, Hq+2Hkv, D] projection
+    output (row stride larger than the K/V row)."""
+    ric, runner = rt
+    w = workloads.get("mixed")
+    b, s, ref, order, exp, _ = _compile(rt, w)
+    n = exp["n_pad"]
+    H, D = w.kv_heads, w.head_dim
+    qkv = torch.randn((n, 32 + 2 * H, D), device="cuda").to(torch.bfloat16)
+    k = qkv[:, 32:32 + H, :]
+    v = qkv[:, 32 + H:, :]
+    kc, vc = runner.alloc_caches(w, fill=0x0101)
+    kv = runner.KVSet([k], [v], kc, vc, w.row_bytes, w.num_kv_blocks * w.block_size)
+    runner.reshape_and_cache(kv, s.slot_mapping, n)
+    torch.cuda.synchronize()
+    slots = torch.from_numpy(exp["slot_mapping"][: exp["num_actual_tokens"]]).cuda()
+    flat_k = kc[0].view(torch.int16).reshape(-1, H * D)
+    flat_v = vc[0].view(torch.int16).reshape(-1, H * D)
+    N = exp["num_actual_tokens"]
+    assert torch.equal(flat_k[slots], k[:N].reshape(N, -1).view(torch.int16))
+    assert torch.equal(flat_v[slots], v[:N].reshape(N, -1).view(torch.int16))
+    b.close()
