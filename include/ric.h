@@ -89,7 +89,11 @@ typedef struct {
     int32_t* sample_indices;   /* logits_indices of the rows with discard == 0, in row order; -1 after */
     int32_t* dev_scalars;      /* [8] device: R, N, N_pad, max_query_len, max_seq_len, num_sampled,
                                   [6] tokens whose column data was out of range since creation
-                                  (always 0 unless device memory was corrupted), [7] unused */
+                                  (always 0 unless device memory was corrupted), [7] sampled
+                                  tokens whose source index was out of range since creation */
+    int32_t* cu_seqlens_k;     /* [i] running total of seq_lens: key-side boundaries of a varlen
+                                  attention call ([P5 prepare_prefill], Q&A item 8); entries past R
+                                  hold the total.  [max_num_reqs + 1]                              */
     /* host values of this step (from the host mirror of the counters) */
     int32_t num_reqs;          /* R */
     int32_t num_actual_tokens; /* N = sum of q */
@@ -184,6 +188,28 @@ int ric_condense(ric_batch* b, int32_t* out_num_moved);
 
 /* Upload staged deltas now. */
 int ric_flush(ric_batch* b);
+
+/* Append one token per listed row from a DEVICE array: last step's sampled ids
+ * stay on the GPU instead of travelling to the host and back; rows are matched
+ * to sample positions by a current-row -> previous-position map
+ * ([P1 §先拷 block table，再做 CPU 索引], the async-scheduling input path).
+ *   rows       HOST int32[n]: live rows receiving a token, each at most once
+ *   src_index  HOST int32[n]: row rows[k] takes dev_tokens[src_index[k]]
+ *              (NULL: dev_tokens[k])
+ *   dev_tokens DEVICE int32[dev_tokens_len], ready on the handle's stream
+ * Each listed row's token count grows by one at once on the host; the values
+ * are written on the device (this call flushes staged deltas).  Errors: EINVAL
+ * (row not live or repeated, index out of range), EFULL (history full). */
+int ric_append_sampled(ric_batch* b, int32_t n, const int32_t* rows, const int32_t* src_index,
+                       const int32_t* dev_tokens, int32_t dev_tokens_len);
+
+/* Dense block table for an attention call that wants one: rows 0..R-1 of the
+ * scheduled batch, `width` entries each, entries past a row's own blocks set
+ * to `fill` (nano-vllm pads with -1, [P5 prepare_block_tables]).  dst: DEVICE
+ * int32[R][width].  The persistent table itself (ric_get_columns) can be used
+ * directly when stale entries past each row's count are acceptable.
+ * Errors: ESTATE (no schedule since the last row change), EINVAL. */
+int ric_block_table_padded(ric_batch* b, int32_t width, int32_t fill, int32_t* dst);
 
 /* Number of live requests; row of a request (or RIC_ENOENT); request at a row
  * (RIC_ENOENT for a hole). */

@@ -124,8 +124,14 @@ def compile_step(rows, *, block_size: int, max_num_reqs: int, max_model_len: int
         discard.append(1)
     sample_indices += [-1] * (max_num_reqs - num_sampled)
 
+    # Key-side boundaries for a varlen attention call: running total of the
+    # sequence lengths ([P5 prepare_prefill], Q&A item 8); pseudo-requests add 0.
+    cu_seqlens_k = [0]
+    for i in range(max_num_reqs):
+        cu_seqlens_k.append(cu_seqlens_k[-1] + seq_lens[i])
+
     return dict(
-        query_start_loc=qsl, seq_lens=seq_lens, logits_indices=logits_indices,
+        query_start_loc=qsl, seq_lens=seq_lens, cu_seqlens_k=cu_seqlens_k, logits_indices=logits_indices,
         discard=discard, sample_indices=sample_indices, num_sampled=num_sampled,
         input_ids=input_ids, positions=positions, req_indices=req_indices,
         slot_mapping=slot_mapping, num_reqs=R, num_actual_tokens=N, num_tokens_padded=n_pad,
@@ -141,6 +147,25 @@ def reshape_and_cache(k_rows, v_rows, k_cache, v_cache, slot_mapping) -> None:
     for t, s in enumerate(slot_mapping):
         k_cache[s] = k_rows[t]
         v_cache[s] = v_rows[t]
+
+
+def padded_block_table(rows, width: int, fill: int = -1):
+    """Rows 0..R-1 of the block table cut or padded to ``width`` entries with
+    ``fill`` past each row's own blocks (nano-vllm's prepare_block_tables pads
+    with -1 to the longest row) [P5 prepare_block_tables]."""
+    out = []
+    for r in rows:
+        out.append([int(r.blocks[j]) if j < len(r.blocks) else fill for j in range(width)])
+    return out
+
+
+def append_sampled(rows_tokens, rows, src_index, sampled):
+    """Append one sampled token per listed row: row rows[k] gets
+    sampled[src_index[k]] at the end of its history (the async-scheduling
+    input path keeps last step's sampled ids on the device and places them
+    through a current-row -> previous-position map, [P1 §先拷 block table，再做 CPU 索引])."""
+    for k, row in enumerate(rows):
+        rows_tokens[row].append(int(sampled[src_index[k] if src_index is not None else k]))
 
 
 def gather_rows(src_rows, indices, count: int, zero_row):

@@ -61,7 +61,8 @@ def compile_arrays(c, q, P, token_table, block_table, *, block_size: int,
     keep = logits[:R][discard[:R] == 0]
     sample = np.full(max_num_reqs, -1, np.int64)
     sample[:keep.shape[0]] = keep
-    out.update(query_start_loc=qsl, seq_lens=seq, logits_indices=logits, discard=discard,
+    cu_k = np.concatenate([[0], np.cumsum(seq)])
+    out.update(query_start_loc=qsl, seq_lens=seq, cu_seqlens_k=cu_k, logits_indices=logits, discard=discard,
                sample_indices=sample, num_sampled=int(keep.shape[0]))
     return {k: (v.astype(np.int64) if isinstance(v, np.ndarray) else v) for k, v in out.items()}
 

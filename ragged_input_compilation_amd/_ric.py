@@ -44,7 +44,7 @@ class ric_sampling(ctypes.Structure):
 class ric_step(ctypes.Structure):
     _fields_ = [("input_ids", _vp), ("positions", _vp), ("req_indices", _vp), ("slot_mapping", _vp),
                 ("query_start_loc", _vp), ("seq_lens", _vp), ("logits_indices", _vp), ("discard", _vp),
-                ("sample_indices", _vp), ("dev_scalars", _vp)] + \
+                ("sample_indices", _vp), ("dev_scalars", _vp), ("cu_seqlens_k", _vp)] + \
                [(n, ctypes.c_int32) for n in ("num_reqs", "num_actual_tokens", "num_tokens_padded",
                                               "max_query_len", "max_seq_len", "num_sampled")]
 
@@ -77,6 +77,8 @@ def _load():
         "ric_replace_blocks": (ctypes.c_int, [_vp, ctypes.c_uint64, _i32p, ctypes.c_int32]),
         "ric_condense": (ctypes.c_int, [_vp, _i32p]),
         "ric_flush": (ctypes.c_int, [_vp]),
+        "ric_append_sampled": (ctypes.c_int, [_vp, ctypes.c_int32, _i32p, _i32p, _vp, ctypes.c_int32]),
+        "ric_block_table_padded": (ctypes.c_int, [_vp, ctypes.c_int32, ctypes.c_int32, _vp]),
         "ric_num_reqs": (ctypes.c_int32, [_vp]),
         "ric_row_of": (ctypes.c_int32, [_vp, ctypes.c_uint64]),
         "ric_req_at": (ctypes.c_int, [_vp, ctypes.c_int32, ctypes.POINTER(ctypes.c_uint64)]),
@@ -197,6 +199,21 @@ def ric_condense(h: int) -> int:
 
 def ric_flush(h: int) -> None:
     _err(_lib.ric_flush(_vp(h)))
+
+
+def ric_append_sampled(h: int, rows, dev_tokens: int, dev_tokens_len: int, src_index=None) -> None:
+    r, rp = _i32(rows)
+    if src_index is None:
+        sp = None
+    else:
+        s, sp = _i32(src_index)
+        if s.shape != r.shape:
+            raise ValueError("rows and src_index differ in length")
+    _err(_lib.ric_append_sampled(_vp(h), r.shape[0], rp, sp, _vp(dev_tokens), dev_tokens_len))
+
+
+def ric_block_table_padded(h: int, width: int, fill: int, dst: int) -> None:
+    _err(_lib.ric_block_table_padded(_vp(h), width, fill, _vp(dst or None)))
 
 
 def ric_num_reqs(h: int) -> int:

@@ -66,7 +66,8 @@ int ilog2_exact(int64_t x) {
 struct Layout {
     int64_t tok_stride, blk_stride;
     size_t off_tok, off_blk, off_scal, off_ids, off_pos, off_req, off_slot, off_qsl, off_seq,
-        off_logits, off_sample, off_discard, off_dscal, off_pairs, off_staging, total;
+        off_logits, off_sample, off_discard, off_dscal, off_pairs, off_cuk, off_samp_off, off_samp_idx,
+        off_staging, total;
     size_t staging_bytes;
 };
 
@@ -107,6 +108,9 @@ Layout layout_of(const ric_config& c) {
     L.off_discard = take(R);
     L.off_dscal = take(kNumDevScalars * 4);
     L.off_pairs = take(R * 2 * 4);
+    L.off_cuk = take((R + 1) * 4);
+    L.off_samp_off = take(R * 8);
+    L.off_samp_idx = take(R * 4);
     L.off_staging = take(L.staging_bytes);
     L.total = o;
     return L;
@@ -145,7 +149,8 @@ struct ric_batch {
     int32_t *d_ids = nullptr, *d_pos = nullptr, *d_req = nullptr, *d_slot = nullptr;
     int32_t *d_qsl = nullptr, *d_seq = nullptr, *d_logits = nullptr, *d_sample = nullptr;
     uint8_t* d_discard = nullptr;
-    int32_t *d_dscal = nullptr, *d_pairs = nullptr;
+    int32_t *d_dscal = nullptr, *d_pairs = nullptr, *d_cuk = nullptr, *d_samp_idx = nullptr;
+    int64_t* d_samp_off = nullptr;
     uint8_t* d_staging = nullptr;
 
     // pinned delta logs
@@ -394,6 +399,9 @@ int ric_create(const ric_config* cfg, void* stream, void* workspace, size_t work
     b->d_discard = b->ws + L.off_discard;
     b->d_dscal = reinterpret_cast<int32_t*>(b->ws + L.off_dscal);
     b->d_pairs = reinterpret_cast<int32_t*>(b->ws + L.off_pairs);
+    b->d_cuk = reinterpret_cast<int32_t*>(b->ws + L.off_cuk);
+    b->d_samp_off = reinterpret_cast<int64_t*>(b->ws + L.off_samp_off);
+    b->d_samp_idx = reinterpret_cast<int32_t*>(b->ws + L.off_samp_idx);
     b->d_staging = b->ws + L.off_staging;
     for (int i = 0; i < 2; ++i) {
         void* p = nullptr;
@@ -613,6 +621,63 @@ int ric_condense(ric_batch* b, int32_t* out_num_moved) {
     return RIC_OK;
 }
 
+int ric_append_sampled(ric_batch* b, int32_t n, const int32_t* rows, const int32_t* src_index,
+                       const int32_t* dev_tokens, int32_t dev_tokens_len) {
+    if (!b) return fail(RIC_EINVAL, "handle is NULL");
+    if (n < 0 || n > b->cfg.max_num_reqs) return fail(RIC_EINVAL, "n %d outside [0, max_num_reqs]", n);
+    if (n == 0) return RIC_OK;
+    if (!rows || !dev_tokens || dev_tokens_len <= 0) return fail(RIC_EINVAL, "NULL or empty argument");
+    std::vector<uint8_t> seen(b->cfg.max_num_reqs, 0);
+    std::vector<int64_t> off((size_t)n);
+    std::vector<int32_t> idx((size_t)n);
+    for (int32_t k = 0; k < n; ++k) {
+        const int32_t r = rows[k];
+        if (r < 0 || r >= b->cfg.max_num_reqs || !b->live[r]) return fail(RIC_EINVAL, "row %d is not live", r);
+        if (seen[r]) return fail(RIC_EINVAL, "row %d listed twice", r);
+        seen[r] = 1;
+        const int32_t T = b->S(kNumTokens, r);
+        if (T + 1 > b->cfg.max_model_len) return fail(RIC_EFULL, "row %d: token history full", r);
+        idx[k] = src_index ? src_index[k] : k;
+        if (idx[k] < 0 || idx[k] >= dev_tokens_len)
+            return fail(RIC_EINVAL, "source index %d outside [0, %d)", idx[k], dev_tokens_len);
+        off[k] = (int64_t)r * b->L.tok_stride + T;
+    }
+    int rc = stage(b, b->d_samp_off, off.data(), 2 * (size_t)n);
+    if (rc) return rc;
+    rc = stage(b, b->d_samp_idx, idx.data(), (size_t)n);
+    if (rc) return rc;
+    for (int32_t k = 0; k < n; ++k) {
+        b->S(kNumTokens, rows[k]) += 1;
+        b->mark(kNumTokens, rows[k]);
+    }
+    b->scheduled = false;
+    rc = flush(b);
+    if (rc) return rc;
+    HIP_TRY(launch_append_sampled(b->d_tok, b->d_samp_off, b->d_samp_idx, dev_tokens, dev_tokens_len, n,
+                                  b->d_dscal + 7, b->stream));
+    return RIC_OK;
+}
+
+int ric_block_table_padded(ric_batch* b, int32_t width, int32_t fill, int32_t* dst) {
+    if (!b) return fail(RIC_EINVAL, "handle is NULL");
+    if (!b->scheduled) return fail(RIC_ESTATE, "ric_schedule must follow the last row change");
+    if (width < 0 || width > b->cfg.max_blocks_per_req)
+        return fail(RIC_EINVAL, "width %d outside [0, max_blocks_per_req %d]", width, b->cfg.max_blocks_per_req);
+    if (width > 0 && b->sched_R > 0 && !dst) return fail(RIC_EINVAL, "dst is NULL");
+    int rc = flush(b);
+    if (rc) return rc;
+    PaddedTableParams p{};
+    p.blocks = b->d_blk;
+    p.num_blocks = b->dcol(kNumBlocks);
+    p.dst = dst;
+    p.blk_stride = b->L.blk_stride;
+    p.rows = b->sched_R;
+    p.width = width;
+    p.fill = fill;
+    HIP_TRY(launch_padded_table(p, b->stream));
+    return RIC_OK;
+}
+
 int ric_flush(ric_batch* b) {
     if (!b) return fail(RIC_EINVAL, "handle is NULL");
     return flush(b);
@@ -749,6 +814,7 @@ int ric_compile(ric_batch* b, int32_t n_pad, ric_step* out) {
     p.discard = b->d_discard;
     p.sample_indices = b->d_sample;
     p.dev_scalars = b->d_dscal;
+    p.cu_seqlens_k = b->d_cuk;
     HIP_TRY(launch_compile(p, b->stream));
     if (out) {
         out->input_ids = b->d_ids;
@@ -761,6 +827,7 @@ int ric_compile(ric_batch* b, int32_t n_pad, ric_step* out) {
         out->discard = b->d_discard;
         out->sample_indices = b->d_sample;
         out->dev_scalars = b->d_dscal;
+        out->cu_seqlens_k = b->d_cuk;
         out->num_reqs = b->sched_R;
         out->num_actual_tokens = b->sched_N;
         out->num_tokens_padded = n_pad;

@@ -55,6 +55,17 @@ struct CompileParams {
     uint8_t* discard;
     int32_t* sample_indices;
     int32_t* dev_scalars;
+    int32_t* cu_seqlens_k;
+};
+
+struct PaddedTableParams {
+    const int32_t* blocks;        // [max_num_reqs][blk_stride]
+    const int32_t* num_blocks;    // device column
+    int32_t* dst;                 // [rows][width]
+    int64_t blk_stride;
+    int32_t rows;
+    int32_t width;
+    int32_t fill;
 };
 
 struct KVParams {
@@ -103,6 +114,10 @@ hipError_t launch_kv_scatter(const KVParams& p, int num_layers, hipStream_t s);
 hipError_t launch_gather(const GatherParams& p, hipStream_t s);
 hipError_t launch_move_rows(const MoveParams& p, int max_token_chunks, hipStream_t s);
 hipError_t launch_apply_deltas(const uint32_t* payload, const DeltaOp* ops, int n_ops, hipStream_t s);
+hipError_t launch_padded_table(const PaddedTableParams& p, hipStream_t s);
+// dst_off[k] (int64, in int32 elements of the token table) <- src[src_idx[k]]
+hipError_t launch_append_sampled(int32_t* tokens, const int64_t* dst_off, const int32_t* src_idx,
+                                 const int32_t* src, int32_t src_len, int32_t n, int32_t* err, hipStream_t s);
 
 // Token tile of one compile workgroup.
 constexpr int kCompileThreads = 256;

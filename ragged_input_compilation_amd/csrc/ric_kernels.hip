@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kCompileThreads) void compile_kernel(CompileParams 
     const int per = (R + kCompileThreads - 1) / kCompileThreads;
     const int r0 = min(R, tid * per);
     const int r1 = min(R, r0 + per);
-    int local = 0, kept = 0, max_q = 0, max_seq = 0;
+    int local = 0, kept = 0, max_q = 0, max_seq = 0, local_seq = 0;
     uint32_t partial = 0;   // bit k: request r0 + k has not reached the end of its prompt
     for (int i = r0; i < r1; ++i) {
         const int q = col_q[i];
@@ -122,6 +122,7 @@ __global__ __launch_bounds__(kCompileThreads) void compile_kernel(CompileParams 
             kept += part ? 0 : 1;
             max_q = max(max_q, q);
             max_seq = max(max_seq, seq);
+            local_seq += seq;
         }
     }
     int N = 0;
@@ -182,21 +183,27 @@ __global__ __launch_bounds__(kCompileThreads) void compile_kernel(CompileParams 
 
     // Per-request outputs (one workgroup).
     const int MR = p.max_num_reqs;
-    int num_sampled = 0;
+    int num_sampled = 0, seq_total = 0;
     int slot_out = block_exclusive_scan<kCompileThreads>(kept, s_tmp, &num_sampled);
+    // key-side boundaries of a varlen attention call: running total of seq_lens
+    int seq_run = block_exclusive_scan<kCompileThreads>(local_seq, s_tmp, &seq_total);
     max_q = block_max<kCompileThreads>(max_q, s_tmp);
     max_seq = block_max<kCompileThreads>(max_seq, s_tmp);
     for (int i = r0; i < r1; ++i) {
         const int end = s_qsl[i + 1];
         const int li = end - 1;
+        const int seq = s_base[i] + end;   // c_i + q_i
         const bool part = ((partial >> (i - r0)) & 1u) != 0;
-        p.seq_lens[i] = s_base[i] + end;   // c_i + q_i
+        p.seq_lens[i] = seq;
+        p.cu_seqlens_k[i] = seq_run;
+        seq_run += seq;
         p.logits_indices[i] = li;
         p.discard[i] = part ? 1 : 0;
         if (!part) p.sample_indices[slot_out++] = li;
     }
     for (int i = tid; i <= MR; i += kCompileThreads) {
         p.query_start_loc[i] = (i <= R) ? s_qsl[i] : N;
+        if (i >= R) p.cu_seqlens_k[i] = seq_total;
         if (i >= R && i < MR) {
             p.seq_lens[i] = 0;
             p.logits_indices[i] = -1;
@@ -448,6 +455,52 @@ __global__ __launch_bounds__(256) void apply_deltas_kernel(const uint32_t* paylo
 hipError_t launch_apply_deltas(const uint32_t* payload, const DeltaOp* ops, int n_ops, hipStream_t s) {
     if (n_ops == 0) return hipSuccess;
     hipLaunchKernelGGL(apply_deltas_kernel, dim3(n_ops), dim3(256), 0, s, payload, ops);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Block table cut or padded to a fixed width for an attention call that wants
+// a dense [rows][width] table: entries past a row's own blocks get `fill`
+// (nano-vllm pads with -1 to the longest row).  blockIdx.y = row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void padded_table_kernel(PaddedTableParams p) {
+    const int r = blockIdx.y;
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    if (j >= p.width) return;
+    const int nb = min((int64_t)p.num_blocks[r], p.blk_stride);
+    p.dst[(int64_t)r * p.width + j] = (j < nb) ? p.blocks[(int64_t)r * p.blk_stride + j] : p.fill;
+}
+
+hipError_t launch_padded_table(const PaddedTableParams& p, hipStream_t s) {
+    if (p.rows == 0 || p.width == 0) return hipSuccess;
+    hipLaunchKernelGGL(padded_table_kernel, dim3((p.width + 255) / 256, p.rows), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Sampled tokens appended on the device: token table element dst_off[k]
+// receives src[src_idx[k]] (last step's sampled ids stay on the GPU and are
+// placed through a current-row -> sample-position map, [P1 §先拷 block table，
+// 再做 CPU 索引]).  An index outside [0, src_len) writes nothing and bumps *err.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void append_sampled_kernel(int32_t* tokens, const int64_t* dst_off,
+                                                             const int32_t* src_idx, const int32_t* src,
+                                                             int32_t src_len, int32_t n, int32_t* err) {
+    const int k = blockIdx.x * 256 + threadIdx.x;
+    if (k >= n) return;
+    const int i = src_idx[k];
+    if (i < 0 || i >= src_len) {
+        atomicAdd(err, 1);
+        return;
+    }
+    tokens[dst_off[k]] = src[i];
+}
+
+hipError_t launch_append_sampled(int32_t* tokens, const int64_t* dst_off, const int32_t* src_idx,
+                                 const int32_t* src, int32_t src_len, int32_t n, int32_t* err, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(append_sampled_kernel, dim3((n + 255) / 256), dim3(256), 0, s, tokens, dst_off, src_idx,
+                       src, src_len, n, err);
     return hipGetLastError();
 }
 

@@ -111,6 +111,7 @@ class Batch:
             "req_indices": self.device_i32(s.req_indices, n),
             "slot_mapping": self.device_i32(s.slot_mapping, n),
             "query_start_loc": self.device_i32(s.query_start_loc, MR + 1),
+            "cu_seqlens_k": self.device_i32(s.cu_seqlens_k, MR + 1),
             "seq_lens": self.device_i32(s.seq_lens, MR),
             "logits_indices": self.device_i32(s.logits_indices, MR),
             "discard": self.device_u8(s.discard, MR),

@@ -49,7 +49,7 @@ def rows_of(reqs):
 
 
 KEYS = ("input_ids", "positions", "req_indices", "slot_mapping", "query_start_loc",
-        "seq_lens", "logits_indices", "discard", "sample_indices")
+        "seq_lens", "cu_seqlens_k", "logits_indices", "discard", "sample_indices")
 
 
 def run_all(rows, *, block_size, max_num_reqs=None, n_pad=None, null_block=0,
@@ -79,7 +79,6 @@ def run_all(rows, *, block_size, max_num_reqs=None, n_pad=None, null_block=0,
     out[0]["max_query_len"] = py["max_query_len"]
     out[0]["max_seq_len"] = py["max_seq_len"]
     out[0]["num_actual_tokens"] = py["num_actual_tokens"]
-    out[2]["cu_seqlens_k"] = np.asarray(cc["cu_seqlens_k"], np.int64)
     out[2]["max_query_len"] = cc["max_query_len"]
     out[2]["max_seq_len"] = cc["max_seq_len"]
     return out

@@ -1,0 +1,114 @@
+"""GPU parity for the rows after the core path: dense padded block tables and
+the device-side append of sampled tokens (async-scheduling input path).
+cu_seqlens_k is compared with every compile in test_gpu_parity.py."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import batch as ref_batch, step as ref_step
+from tests.gpu_helpers import expected_step, replay_history
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def rt():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from ragged_input_compilation_amd import _ric, runner
+    return _ric, runner
+
+
+@pytest.mark.parametrize("name", ["mixed", "churn", "worked_example"])
+def test_padded_block_table(rt, name):
+    ric, runner = rt
+    w = workloads.get(name)
+    b = runner.Batch(runner.config_of(w))
+    b.load_history(w)
+    ref, order = replay_history(w)
+    b.schedule_from(w, order)
+    rows = ref.step_rows()
+    width = min(max(len(r.blocks) for r in rows) + 3, w.max_blocks_per_req)
+    want = np.asarray(ref_step.padded_block_table(rows, width), np.int32)
+    dst = torch.full((len(rows), width), 12345, dtype=torch.int32, device="cuda")
+    ric.ric_block_table_padded(b.h, width, -1, dst.data_ptr())
+    torch.cuda.synchronize()
+    assert np.array_equal(dst.cpu().numpy(), want)
+    narrow = max(1, width // 3)
+    dst2 = torch.zeros((len(rows), narrow), dtype=torch.int32, device="cuda")
+    ric.ric_block_table_padded(b.h, narrow, 0, dst2.data_ptr())
+    torch.cuda.synchronize()
+    assert np.array_equal(dst2.cpu().numpy(), np.asarray(ref_step.padded_block_table(rows, narrow, 0), np.int32))
+    b.close()
+
+
+def test_padded_block_table_needs_a_schedule(rt):
+    ric, runner = rt
+    w = workloads.get("worked_example")
+    b = runner.Batch(runner.config_of(w))
+    b.load_history(w)
+    with pytest.raises(ric.RicError) as e:
+        ric.ric_block_table_padded(b.h, 4, -1, 0)
+    assert e.value.code == ric.RIC_ESTATE
+    b.close()
+
+
+def test_append_sampled_decode_loop(rt):
+    """Twelve decode steps where last step's sampled ids (a device array in
+    sample order) are appended through a row -> sample-position map, with a
+    request finishing and the batch condensed midway.  Every step's compile
+    equals the oracle's, whose histories got the same ids on the host."""
+    ric, runner = rt
+    rng = np.random.default_rng(21)
+    B, MR, M = 16, 16, 256
+    cfg = ric.make_config(max_num_reqs=MR, max_model_len=M, block_size=B, max_blocks_per_req=M // B,
+                          max_num_batched_tokens=64, num_kv_blocks=2048, null_block=0, staging_bytes=0)
+    b = runner.Batch(cfg)
+    ref = ref_batch.RefBatch(MR, M, M // B, 2048)
+    free = list(rng.permutation(np.arange(1, 2048)))
+    for rid in range(10):
+        T = int(rng.integers(3, 60))
+        toks = rng.integers(0, 50000, T)
+        blks = [int(free.pop()) for _ in range(-(-(T + 20) // B))]
+        ric.ric_add_request(b.h, rid, toks, T, T - 1, blks)
+        ref.add_request(rid, toks, T, T - 1, blks)
+    prev_sample_pos = None      # request id -> position in last step's sampled array
+    sampled_host = None
+    sampled_dev = None
+    for step_no in range(12):
+        if step_no == 5:
+            for rid in (2, 7):
+                ric.ric_remove_request(b.h, rid)
+                ref.remove_request(rid)
+            ric.ric_condense(b.h)
+            ref.condense()
+        order = [rid for rid in ref.req_ids_by_row() if rid is not None]
+        assert b.row_order() == order
+        if sampled_dev is not None:
+            rows = [i for i, rid in enumerate(order) if rid in prev_sample_pos]
+            src = [prev_sample_pos[order[i]] for i in rows]
+            ric.ric_append_sampled(b.h, rows, sampled_dev.data_ptr(), sampled_dev.numel(), src)
+            for i, j in zip(rows, src):
+                ref.append_tokens(order[i], [int(sampled_host[j])])
+        c = [len(ref.rows[i].tokens) - 1 for i in range(len(order))]
+        ric.ric_schedule(b.h, c, [1] * len(order))
+        ref.schedule(c, [1] * len(order))
+        want = ref_step.compile_step(ref.step_rows(), block_size=B, max_num_reqs=MR, max_model_len=M,
+                                     max_num_batched_tokens=64, num_kv_blocks=2048, n_pad=len(order))
+        s = b.compile(len(order))
+        got = b.step_outputs(s)
+        for k in ("input_ids", "positions", "slot_mapping", "seq_lens", "cu_seqlens_k", "query_start_loc"):
+            assert np.array_equal(np.asarray(got[k], np.int64), np.asarray(want[k], np.int64)), (step_no, k)
+        assert int(got["dev_scalars"][7]) == 0
+        # "sample": one new id per request; request order[i]'s id sits at
+        # position perm[i] of the device array (a sampler's own order)
+        perm = rng.permutation(len(order))
+        sampled_host = rng.integers(0, 50000, len(order)).astype(np.int32)
+        sampled_dev = torch.from_numpy(sampled_host).cuda()
+        prev_sample_pos = {order[i]: int(perm[i]) for i in range(len(order))}
+    with pytest.raises(ric.RicError):
+        ric.ric_append_sampled(b.h, [0, 0], sampled_dev.data_ptr(), sampled_dev.numel(), [0, 1])
+    with pytest.raises(ric.RicError):
+        ric.ric_append_sampled(b.h, [0], sampled_dev.data_ptr(), sampled_dev.numel(), [99])
+    b.close()

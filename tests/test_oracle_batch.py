@@ -168,6 +168,34 @@ def test_kv_write_three_ways_agree():
             assert np.array_equal(np.delete(kc, np.arange(B), 0), np.delete(caches[0][0], np.arange(B), 0))
 
 
+def test_padded_block_table_definition():
+    """nano-vllm pads each request's block list with -1 to the longest one
+    (prepare_block_tables); width may also cut a row."""
+    from tests.oracle_helpers import Row
+    rows = [Row(0, 1, 1, np.arange(3), np.array([4, 5, 9])), Row(0, 1, 1, np.arange(3), np.array([7])),
+            Row(0, 1, 1, np.arange(3), np.array([], np.int64))]
+    assert step.padded_block_table(rows, 3) == [[4, 5, 9], [7, -1, -1], [-1, -1, -1]]
+    assert step.padded_block_table(rows, 2, fill=0) == [[4, 5], [7, 0], [0, 0]]
+
+
+def test_append_sampled_then_decode():
+    """Appending last step's sampled ids through a row -> sample-position map
+    and then compiling one decode token per row feeds exactly those ids."""
+    b = _mk()
+    for k in range(5):
+        b.add_request(k, [100 + k] * (k + 2), k + 2, k + 2, [k + 1])
+    sampled = [900, 901, 902, 903, 904]
+    src = [4, 2, 0, 1, 3]                  # the batch was reordered since sampling
+    toks = {i: b.rows[i].tokens for i in range(5)}
+    step.append_sampled(toks, list(range(5)), src, sampled)
+    T = [len(b.rows[i].tokens) for i in range(5)]
+    b.schedule([t - 1 for t in T], [1] * 5)
+    out = step.compile_step(b.step_rows(), block_size=16, max_num_reqs=8, max_model_len=64,
+                            max_num_batched_tokens=8, num_kv_blocks=100, n_pad=5)
+    assert out["input_ids"] == [sampled[j] for j in src]
+    assert out["positions"] == [t - 1 for t in T]
+
+
 def test_gather_three_ways_agree():
     rng = np.random.default_rng(3)
     src = rng.integers(0, 256, size=(50, 24), dtype=np.uint8)
