@@ -203,6 +203,33 @@ int ric_flush(ric_batch* b);
 int ric_append_sampled(ric_batch* b, int32_t n, const int32_t* rows, const int32_t* src_index,
                        const int32_t* dev_tokens, int32_t dev_tokens_len);
 
+/* Logits positions when requests carry draft tokens (speculative decoding,
+ * [P1 §投机解码：一条请求一轮可能产生多个决策位置], [P2 §8.6.3]).  Row i verifies
+ * d_i = num_draft_tokens[i] drafts, which are its last d_i scheduled tokens
+ * (d_i + 1 <= q_i).  Its logits are needed at its last d_i + 1 flat
+ * positions: the first d_i of those rows check the drafts, the last gives the
+ * bonus token.  All arrays are device, owned by the handle, stable:
+ *   logits_indices[num_logits]        flat positions, request by request
+ *   cu_num_logits[R+1]                running total of (d_i + 1)
+ *   target_logits_indices[num_draft]  logits row that checks each draft
+ *   bonus_logits_indices[R]           logits row of each request's bonus token
+ *   draft_token_ids[num_draft]        the draft ids (from input_ids)
+ * With all d_i = 0 logits_indices equals ric_step.logits_indices[0..R). */
+typedef struct {
+    int32_t* logits_indices;
+    int32_t* cu_num_logits;
+    int32_t* target_logits_indices;
+    int32_t* bonus_logits_indices;
+    int32_t* draft_token_ids;
+    int32_t num_logits;        /* sum of (d_i + 1) */
+    int32_t num_draft_tokens;  /* sum of d_i */
+} ric_spec_decode;
+
+/* Build the speculative-decoding indices for the last compiled step from HOST
+ * draft counts num_draft_tokens[R].  Errors: ESTATE (no compile of the current
+ * schedule), EINVAL (d_i < 0 or d_i + 1 > q_i). */
+int ric_spec_decode_metadata(ric_batch* b, const int32_t* num_draft_tokens, ric_spec_decode* out);
+
 /* Dense block table for an attention call that wants one: rows 0..R-1 of the
  * scheduled batch, `width` entries each, entries past a row's own blocks set
  * to `fill` (nano-vllm pads with -1, [P5 prepare_block_tables]).  dst: DEVICE

@@ -149,6 +149,30 @@ def reshape_and_cache(k_rows, v_rows, k_cache, v_cache, slot_mapping) -> None:
         v_cache[s] = v_rows[t]
 
 
+def spec_decode_metadata(query_start_loc, input_ids, num_draft_tokens):
+    """Logits positions when requests carry draft tokens.
+
+    A request verifying d draft tokens needs logits at its last d + 1 flat
+    positions: the rows at its first d of them check the drafts, the last one
+    gives the bonus token; the drafts themselves are its last d input ids
+    ([P1 §投机解码：一条请求一轮可能产生多个决策位置]; [P2 §8.6.3]).  With no
+    drafts this is query_start_loc[1:] - 1.  Returns a dict of lists; indices
+    into the logits rows are "target" (one per draft) and "bonus" (one per
+    request)."""
+    logits, cu, target, bonus, drafts = [], [0], [], [], []
+    for i, d in enumerate(num_draft_tokens):
+        end = query_start_loc[i + 1]
+        for k in range(d + 1):
+            logits.append(end - (d + 1) + k)
+        for k in range(d):
+            target.append(cu[-1] + k)
+            drafts.append(int(input_ids[end - d + k]))
+        cu.append(cu[-1] + d + 1)
+        bonus.append(cu[-1] - 1)
+    return dict(logits_indices=logits, cu_num_logits=cu, target_logits_indices=target,
+                bonus_logits_indices=bonus, draft_token_ids=drafts)
+
+
 def padded_block_table(rows, width: int, fill: int = -1):
     """Rows 0..R-1 of the block table cut or padded to ``width`` entries with
     ``fill`` past each row's own blocks (nano-vllm's prepare_block_tables pads

@@ -56,6 +56,12 @@ class ric_columns(ctypes.Structure):
                                    "num_blocks", "top_k", "temperature", "top_p", "repetition_penalty")]
 
 
+class ric_spec_decode(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("logits_indices", "cu_num_logits", "target_logits_indices",
+                                   "bonus_logits_indices", "draft_token_ids")] + \
+               [("num_logits", ctypes.c_int32), ("num_draft_tokens", ctypes.c_int32)]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is not built: run `python -m ragged_input_compilation_amd.build` "
@@ -79,6 +85,7 @@ def _load():
         "ric_flush": (ctypes.c_int, [_vp]),
         "ric_append_sampled": (ctypes.c_int, [_vp, ctypes.c_int32, _i32p, _i32p, _vp, ctypes.c_int32]),
         "ric_block_table_padded": (ctypes.c_int, [_vp, ctypes.c_int32, ctypes.c_int32, _vp]),
+        "ric_spec_decode_metadata": (ctypes.c_int, [_vp, _i32p, ctypes.POINTER(ric_spec_decode)]),
         "ric_num_reqs": (ctypes.c_int32, [_vp]),
         "ric_row_of": (ctypes.c_int32, [_vp, ctypes.c_uint64]),
         "ric_req_at": (ctypes.c_int, [_vp, ctypes.c_int32, ctypes.POINTER(ctypes.c_uint64)]),
@@ -210,6 +217,13 @@ def ric_append_sampled(h: int, rows, dev_tokens: int, dev_tokens_len: int, src_i
         if s.shape != r.shape:
             raise ValueError("rows and src_index differ in length")
     _err(_lib.ric_append_sampled(_vp(h), r.shape[0], rp, sp, _vp(dev_tokens), dev_tokens_len))
+
+
+def ric_spec_decode_metadata(h: int, num_draft_tokens) -> ric_spec_decode:
+    d, dp = _i32(num_draft_tokens)
+    out = ric_spec_decode()
+    _err(_lib.ric_spec_decode_metadata(_vp(h), dp, ctypes.byref(out)))
+    return out
 
 
 def ric_block_table_padded(h: int, width: int, fill: int, dst: int) -> None:

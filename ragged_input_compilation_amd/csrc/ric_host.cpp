@@ -67,6 +67,7 @@ struct Layout {
     int64_t tok_stride, blk_stride;
     size_t off_tok, off_blk, off_scal, off_ids, off_pos, off_req, off_slot, off_qsl, off_seq,
         off_logits, off_sample, off_discard, off_dscal, off_pairs, off_cuk, off_samp_off, off_samp_idx,
+        off_spec_logits, off_spec_target, off_spec_draft, off_spec_cu, off_spec_bonus, off_spec_d,
         off_staging, total;
     size_t staging_bytes;
 };
@@ -111,6 +112,12 @@ Layout layout_of(const ric_config& c) {
     L.off_cuk = take((R + 1) * 4);
     L.off_samp_off = take(R * 8);
     L.off_samp_idx = take(R * 4);
+    L.off_spec_logits = take(NT * 4);
+    L.off_spec_target = take(NT * 4);
+    L.off_spec_draft = take(NT * 4);
+    L.off_spec_cu = take((R + 1) * 4);
+    L.off_spec_bonus = take(R * 4);
+    L.off_spec_d = take(R * 4);
     L.off_staging = take(L.staging_bytes);
     L.total = o;
     return L;
@@ -151,6 +158,8 @@ struct ric_batch {
     uint8_t* d_discard = nullptr;
     int32_t *d_dscal = nullptr, *d_pairs = nullptr, *d_cuk = nullptr, *d_samp_idx = nullptr;
     int64_t* d_samp_off = nullptr;
+    int32_t *d_spec_logits = nullptr, *d_spec_target = nullptr, *d_spec_draft = nullptr,
+            *d_spec_cu = nullptr, *d_spec_bonus = nullptr, *d_spec_d = nullptr;
     uint8_t* d_staging = nullptr;
 
     // pinned delta logs
@@ -174,6 +183,7 @@ struct ric_batch {
 
     // schedule state
     bool scheduled = false;
+    bool compiled = false;           // a compile ran since the last schedule
     int32_t sched_R = 0, sched_N = 0, sched_max_q = 0, sched_max_seq = 0, sched_sampled = 0;
 
     int32_t& S(int col, int row) { return scal[(size_t)col * cfg.max_num_reqs + row]; }
@@ -402,6 +412,12 @@ int ric_create(const ric_config* cfg, void* stream, void* workspace, size_t work
     b->d_cuk = reinterpret_cast<int32_t*>(b->ws + L.off_cuk);
     b->d_samp_off = reinterpret_cast<int64_t*>(b->ws + L.off_samp_off);
     b->d_samp_idx = reinterpret_cast<int32_t*>(b->ws + L.off_samp_idx);
+    b->d_spec_logits = reinterpret_cast<int32_t*>(b->ws + L.off_spec_logits);
+    b->d_spec_target = reinterpret_cast<int32_t*>(b->ws + L.off_spec_target);
+    b->d_spec_draft = reinterpret_cast<int32_t*>(b->ws + L.off_spec_draft);
+    b->d_spec_cu = reinterpret_cast<int32_t*>(b->ws + L.off_spec_cu);
+    b->d_spec_bonus = reinterpret_cast<int32_t*>(b->ws + L.off_spec_bonus);
+    b->d_spec_d = reinterpret_cast<int32_t*>(b->ws + L.off_spec_d);
     b->d_staging = b->ws + L.off_staging;
     for (int i = 0; i < 2; ++i) {
         void* p = nullptr;
@@ -658,6 +674,47 @@ int ric_append_sampled(ric_batch* b, int32_t n, const int32_t* rows, const int32
     return RIC_OK;
 }
 
+int ric_spec_decode_metadata(ric_batch* b, const int32_t* num_draft_tokens, ric_spec_decode* out) {
+    if (!b || !out) return fail(RIC_EINVAL, "NULL argument");
+    if (!b->scheduled || !b->compiled) return fail(RIC_ESTATE, "needs a compile of the current schedule");
+    const int32_t R = b->sched_R;
+    if (R > 0 && !num_draft_tokens) return fail(RIC_EINVAL, "num_draft_tokens is NULL");
+    int64_t num_logits = 0, num_draft = 0;
+    for (int32_t i = 0; i < R; ++i) {
+        const int32_t d = num_draft_tokens[i];
+        if (d < 0 || d + 1 > b->S(kNumScheduled, i))
+            return fail(RIC_EINVAL, "row %d: %d drafts need more than its %d scheduled tokens", i, d,
+                        b->S(kNumScheduled, i));
+        num_logits += d + 1;
+        num_draft += d;
+    }
+    int rc = stage(b, b->d_spec_d, num_draft_tokens, (size_t)R);
+    if (rc) return rc;
+    rc = flush(b);
+    if (rc) return rc;
+    SpecParams p{};
+    p.qsl = b->d_qsl;
+    p.input_ids = b->d_ids;
+    p.num_draft = b->d_spec_d;
+    p.num_reqs = R;
+    p.num_logits = (int32_t)num_logits;
+    p.num_tiles = (int32_t)((num_logits + 255) / 256);
+    p.logits_indices = b->d_spec_logits;
+    p.cu_num_logits = b->d_spec_cu;
+    p.target = b->d_spec_target;
+    p.bonus = b->d_spec_bonus;
+    p.draft_ids = b->d_spec_draft;
+    HIP_TRY(launch_spec_decode(p, b->stream));
+    out->logits_indices = b->d_spec_logits;
+    out->cu_num_logits = b->d_spec_cu;
+    out->target_logits_indices = b->d_spec_target;
+    out->bonus_logits_indices = b->d_spec_bonus;
+    out->draft_token_ids = b->d_spec_draft;
+    out->num_logits = (int32_t)num_logits;
+    out->num_draft_tokens = (int32_t)num_draft;
+    return RIC_OK;
+}
+
 int ric_block_table_padded(ric_batch* b, int32_t width, int32_t fill, int32_t* dst) {
     if (!b) return fail(RIC_EINVAL, "handle is NULL");
     if (!b->scheduled) return fail(RIC_ESTATE, "ric_schedule must follow the last row change");
@@ -775,6 +832,7 @@ int ric_schedule(ric_batch* b, int32_t R, const int32_t* c, const int32_t* q) {
         b->mark(kNumScheduled, R - 1);
     }
     b->scheduled = true;
+    b->compiled = false;
     b->sched_R = R;
     b->sched_N = N;
     b->sched_max_q = mq;
@@ -816,6 +874,7 @@ int ric_compile(ric_batch* b, int32_t n_pad, ric_step* out) {
     p.dev_scalars = b->d_dscal;
     p.cu_seqlens_k = b->d_cuk;
     HIP_TRY(launch_compile(p, b->stream));
+    b->compiled = true;
     if (out) {
         out->input_ids = b->d_ids;
         out->positions = b->d_pos;

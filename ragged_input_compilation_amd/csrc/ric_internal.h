@@ -58,6 +58,20 @@ struct CompileParams {
     int32_t* cu_seqlens_k;
 };
 
+struct SpecParams {
+    const int32_t* qsl;           // compile output [R + 1]
+    const int32_t* input_ids;     // compile output
+    const int32_t* num_draft;     // [R] uploaded draft counts
+    int32_t num_reqs;
+    int32_t num_logits;           // sum of (d + 1)
+    int32_t num_tiles;
+    int32_t* logits_indices;      // [num_logits]
+    int32_t* cu_num_logits;       // [R + 1]
+    int32_t* target;              // [sum d]
+    int32_t* bonus;               // [R]
+    int32_t* draft_ids;           // [sum d]
+};
+
 struct PaddedTableParams {
     const int32_t* blocks;        // [max_num_reqs][blk_stride]
     const int32_t* num_blocks;    // device column
@@ -115,6 +129,7 @@ hipError_t launch_gather(const GatherParams& p, hipStream_t s);
 hipError_t launch_move_rows(const MoveParams& p, int max_token_chunks, hipStream_t s);
 hipError_t launch_apply_deltas(const uint32_t* payload, const DeltaOp* ops, int n_ops, hipStream_t s);
 hipError_t launch_padded_table(const PaddedTableParams& p, hipStream_t s);
+hipError_t launch_spec_decode(const SpecParams& p, hipStream_t s);
 // dst_off[k] (int64, in int32 elements of the token table) <- src[src_idx[k]]
 hipError_t launch_append_sampled(int32_t* tokens, const int64_t* dst_off, const int32_t* src_idx,
                                  const int32_t* src, int32_t src_len, int32_t n, int32_t* err, hipStream_t s);

@@ -459,6 +459,72 @@ hipError_t launch_apply_deltas(const uint32_t* payload, const DeltaOp* ops, int 
 }
 
 // ---------------------------------------------------------------------------
+// Speculative decoding: a request verifying d drafts needs logits at its last
+// d + 1 flat positions; the first d of those rows check the drafts (target),
+// the last one gives the bonus token; the drafts are its last d input ids
+// ([P1 §投机解码：一条请求一轮可能产生多个决策位置]).  Every workgroup rebuilds
+// the prefix sum of (d + 1) in LDS; workgroups 0..num_tiles-1 each own 256
+// logits rows; the last workgroup writes cu_num_logits and the bonus rows.
+// Draft offsets need no second scan: sum_{j<i} d_j = cu[i] - i.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void spec_decode_kernel(SpecParams p) {
+    extern __shared__ int32_t smem[];
+    const int R = p.num_reqs;
+    int32_t* s_cu = smem;                 // [R + 1]
+    int32_t* s_tmp = smem + R + 1;        // [4]
+    const int tid = threadIdx.x;
+    const int per = (R + 255) / 256;
+    const int r0 = min(R, tid * per);
+    const int r1 = min(R, r0 + per);
+    int local = 0;
+    for (int i = r0; i < r1; ++i) {
+        const int n = p.num_draft[i] + 1;
+        s_cu[i] = n;
+        local += n;
+    }
+    int total = 0;
+    int run = block_exclusive_scan<256>(local, s_tmp, &total);
+    for (int i = r0; i < r1; ++i) {
+        const int n = s_cu[i];
+        s_cu[i] = run;
+        run += n;
+    }
+    if (tid == 0) s_cu[R] = total;
+    __syncthreads();
+
+    if ((int)blockIdx.x < p.num_tiles) {
+        const int m = blockIdx.x * 256 + tid;
+        if (m >= p.num_logits) return;
+        int lo = 0, hi = R - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_cu[mid] <= m) lo = mid; else hi = mid - 1;
+        }
+        const int r = lo;
+        const int d = s_cu[r + 1] - s_cu[r] - 1;
+        const int k = m - s_cu[r];
+        const int end = p.qsl[r + 1];
+        p.logits_indices[m] = end - (d + 1) + k;
+        if (k < d) {
+            const int j = s_cu[r] - r + k;
+            p.target[j] = m;
+            p.draft_ids[j] = p.input_ids[end - d + k];
+        }
+        return;
+    }
+    for (int i = tid; i <= R; i += 256) {
+        p.cu_num_logits[i] = s_cu[i];
+        if (i < R) p.bonus[i] = s_cu[i + 1] - 1;
+    }
+}
+
+hipError_t launch_spec_decode(const SpecParams& p, hipStream_t s) {
+    const size_t lds = sizeof(int32_t) * ((size_t)p.num_reqs + 1 + 4);
+    hipLaunchKernelGGL(spec_decode_kernel, dim3(p.num_tiles + 1), dim3(256), lds, s, p);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Block table cut or padded to a fixed width for an attention call that wants
 // a dense [rows][width] table: entries past a row's own blocks get `fill`
 // (nano-vllm pads with -1 to the longest row).  blockIdx.y = row.

@@ -112,3 +112,40 @@ def test_append_sampled_decode_loop(rt):
     with pytest.raises(ric.RicError):
         ric.ric_append_sampled(b.h, [0], sampled_dev.data_ptr(), sampled_dev.numel(), [99])
     b.close()
+
+
+@pytest.mark.parametrize("name", ["mixed", "churn", "decode_heavy", "worked_example"])
+def test_spec_decode_metadata(rt, name):
+    """Random draft counts (0..7, at most q-1 per row): every index array
+    equals the oracle's, computed from the oracle's own compile."""
+    ric, runner = rt
+    w = workloads.get(name)
+    b = runner.Batch(runner.config_of(w))
+    b.load_history(w)
+    ref, order = replay_history(w)
+    b.schedule_from(w, order)
+    exp = expected_step(w, ref)
+    with pytest.raises(ric.RicError) as e:
+        ric.ric_spec_decode_metadata(b.h, [0] * len(order))
+    assert e.value.code == ric.RIC_ESTATE
+    b.compile(exp["n_pad"])
+    rng = np.random.default_rng(41)
+    rows = ref.step_rows()
+    for trial in range(3):
+        d = [0] * len(rows) if trial == 0 else \
+            [int(rng.integers(0, min(r.num_scheduled - 1, 7) + 1)) for r in rows]
+        want = ref_step.spec_decode_metadata(exp["query_start_loc"], exp["input_ids"], d)
+        out = ric.ric_spec_decode_metadata(b.h, d)
+        assert (out.num_logits, out.num_draft_tokens) == (len(want["logits_indices"]), sum(d))
+        for key, n in (("logits_indices", out.num_logits), ("cu_num_logits", len(rows) + 1),
+                       ("target_logits_indices", out.num_draft_tokens),
+                       ("bonus_logits_indices", len(rows)), ("draft_token_ids", out.num_draft_tokens)):
+            got = ric.ric_read_device(getattr(out, key), 4 * n, np.int32) if n else np.zeros(0, np.int32)
+            assert np.array_equal(got.astype(np.int64), np.asarray(want[key], np.int64)), (trial, key)
+        if trial == 0:
+            assert np.array_equal(np.asarray(want["logits_indices"]), exp["logits_indices"][:len(rows)])
+    if any(r.num_scheduled == 1 for r in rows):
+        bad = [r.num_scheduled for r in rows]       # d = q: one too many
+        with pytest.raises(ric.RicError):
+            ric.ric_spec_decode_metadata(b.h, bad)
+    b.close()

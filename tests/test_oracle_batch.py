@@ -196,6 +196,44 @@ def test_append_sampled_then_decode():
     assert out["positions"] == [t - 1 for t in T]
 
 
+def test_spec_decode_reduces_to_plain_logits_without_drafts():
+    """No drafts: one logits row per request, at query_start_loc[1:] - 1 (the
+    closed form the second page prints for [0,2,9,12] -> [1,8,11])."""
+    g = golden("p2_logits.json")
+    qsl = g["query_start_loc"]
+    m = step.spec_decode_metadata(qsl, list(range(qsl[-1])), [0, 0, 0])
+    assert m["logits_indices"] == g["expect"]["logits_indices"]
+    assert m["bonus_logits_indices"] == [0, 1, 2] and m["target_logits_indices"] == []
+    assert m["cu_num_logits"] == [0, 1, 2, 3]
+
+
+def test_spec_decode_invariants_bruteforce():
+    """Every logits position lies inside its request and the request's last
+    position is always among them; a request's d drafts are its last d input
+    ids, checked by the rows right before its bonus row."""
+    rng = np.random.default_rng(31)
+    for trial in range(300):
+        R = int(rng.integers(1, 6))
+        q = rng.integers(1, 7, R)
+        d = [int(rng.integers(0, qi)) for qi in q]          # d + 1 <= q
+        qsl = [0] + list(np.cumsum(q))
+        ids = rng.integers(0, 1000, qsl[-1])
+        m = step.spec_decode_metadata(qsl, ids, d)
+        assert len(m["logits_indices"]) == sum(d) + R and len(m["draft_token_ids"]) == sum(d)
+        pos = 0
+        for i in range(R):
+            rows = m["logits_indices"][m["cu_num_logits"][i]:m["cu_num_logits"][i + 1]]
+            assert rows == list(range(qsl[i + 1] - d[i] - 1, qsl[i + 1]))
+            assert m["bonus_logits_indices"][i] == m["cu_num_logits"][i + 1] - 1
+            assert m["logits_indices"][m["bonus_logits_indices"][i]] == qsl[i + 1] - 1
+            for k in range(d[i]):
+                t = m["target_logits_indices"][pos + k]
+                # the target row for draft k sits at the flat position right before that draft
+                assert m["logits_indices"][t] + 1 == qsl[i + 1] - d[i] + k
+                assert m["draft_token_ids"][pos + k] == ids[qsl[i + 1] - d[i] + k]
+            pos += d[i]
+
+
 def test_gather_three_ways_agree():
     rng = np.random.default_rng(3)
     src = rng.integers(0, 256, size=(50, 24), dtype=np.uint8)
