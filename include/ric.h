@@ -59,8 +59,25 @@ typedef struct {
     int32_t num_kv_blocks;           /* physical blocks in the cache; num_kv_blocks*B < 2^31 */
     int32_t null_block;              /* reserved block for padded tokens (usually 0)      */
     int32_t staging_bytes;           /* pinned delta-staging capacity; 0 = default (4 MiB, more
-                                        for large batches); at least 72*max_num_reqs + 64 KiB */
+                                        for large batches); at least 96*max_num_reqs + 64 KiB */
+    /* KV-cache groups ([P1 §混合 KV Cache：一条请求不止一张页表]): a request can
+     * own one block table per group (full attention, sliding window,
+     * recurrent state...).  Group 0 is described by the fields above; groups
+     * 1..num_kv_groups-1 by these arrays (index g).  Entry 0 of each array is
+     * ignored. */
+    int32_t num_kv_groups;           /* 1..4; 0 means 1 */
+    int32_t group_block_size[4];     /* block size of group g; its table holds
+                                        ceil(max_model_len / block size) entries */
+    int32_t group_num_kv_blocks[4];  /* pool size of group g (0: num_kv_blocks); block
+                                        null_block is reserved in every pool      */
+    int32_t group_slot_mode[4];      /* RIC_SLOTS_PER_TOKEN: compile emits slots for
+                                        group g; RIC_SLOTS_NONE: no slots (e.g. a
+                                        recurrent-state group, SlotMappingMode.NONE) */
 } ric_config;
+
+#define RIC_MAX_KV_GROUPS   4
+#define RIC_SLOTS_PER_TOKEN 0
+#define RIC_SLOTS_NONE      1
 
 /* Per-request sampling values.  They live in the column store and move with
  * their row; sampling itself is not part of this library.  [P2 §8.2.1]. */
@@ -94,6 +111,9 @@ typedef struct {
     int32_t* cu_seqlens_k;     /* [i] running total of seq_lens: key-side boundaries of a varlen
                                   attention call ([P5 prepare_prefill], Q&A item 8); entries past R
                                   hold the total.  [max_num_reqs + 1]                              */
+    int32_t* group_slot_mapping[4]; /* [g] slots of KV-cache group g through its own table and
+                                  block size (pad: null_block * its block size); [0] is
+                                  slot_mapping; NULL for RIC_SLOTS_NONE groups and g >= groups */
     /* host values of this step (from the host mirror of the counters) */
     int32_t num_reqs;          /* R */
     int32_t num_actual_tokens; /* N = sum of q */
@@ -178,6 +198,12 @@ int ric_append_blocks(ric_batch* b, uint64_t req_id, const int32_t* ids, int32_t
  * old ids are no longer valid, [P1 §驻留请求只合并差量]).  Errors as append. */
 int ric_replace_blocks(ric_batch* b, uint64_t req_id, const int32_t* ids, int32_t n);
 
+/* The same two calls for KV-cache group `group` (0 is the calls above).  A new
+ * request's rows in groups >= 1 start empty.  Errors as above, plus EINVAL for
+ * a group outside [0, num_kv_groups). */
+int ric_append_blocks_group(ric_batch* b, uint64_t req_id, int32_t group, const int32_t* ids, int32_t n);
+int ric_replace_blocks_group(ric_batch* b, uint64_t req_id, int32_t group, const int32_t* ids, int32_t n);
+
 /* Fill holes so the live rows are exactly [0, R): the k-th lowest hole
  * receives the k-th highest live row while the hole lies below it, and every
  * column of a moved row moves with it (token history, block row, counters,
@@ -230,13 +256,19 @@ typedef struct {
  * schedule), EINVAL (d_i < 0 or d_i + 1 > q_i). */
 int ric_spec_decode_metadata(ric_batch* b, const int32_t* num_draft_tokens, ric_spec_decode* out);
 
-/* Dense block table for an attention call that wants one: rows 0..R-1 of the
- * scheduled batch, `width` entries each, entries past a row's own blocks set
- * to `fill` (nano-vllm pads with -1, [P5 prepare_block_tables]).  dst: DEVICE
- * int32[R][width].  The persistent table itself (ric_get_columns) can be used
- * directly when stale entries past each row's count are acceptable.
- * Errors: ESTATE (no schedule since the last row change), EINVAL. */
-int ric_block_table_padded(ric_batch* b, int32_t width, int32_t fill, int32_t* dst);
+/* Dense block table of KV-cache group `group` for an attention call that
+ * wants one: rows 0..R-1 of the scheduled batch, `width` entries each.
+ * With kernel_blocks_per_block = k > 1 every stored id m is expanded to the k
+ * kernel block ids m*k .. m*k+k-1 (a manager block of k*Bk tokens over a
+ * kernel of block size Bk, [P1 §混合 KV Cache]: [0,1,2] -> [0..5] for k = 2).
+ * Entries past a row's own (expanded) blocks are set to `fill` (nano-vllm pads
+ * with -1, [P5 prepare_block_tables]).  dst: DEVICE int32[R][width],
+ * width <= k * the group's table capacity.  The persistent table itself
+ * (ric_get_columns, group 0) can be used directly when stale entries past
+ * each row's count are acceptable.  Errors: ESTATE (no schedule since the
+ * last row change), EINVAL. */
+int ric_block_table_padded(ric_batch* b, int32_t group, int32_t kernel_blocks_per_block, int32_t width,
+                           int32_t fill, int32_t* dst);
 
 /* Number of live requests; row of a request (or RIC_ENOENT); request at a row
  * (RIC_ENOENT for a hole). */

@@ -40,6 +40,7 @@ class RowState:
     num_scheduled: int
     blocks: List[int]
     sampling: Tuple[float, float, float, int] = (1.0, 1.0, 1.0, 0)  # temp, top_p, rep, top_k
+    group_blocks: Dict[int, List[int]] = field(default_factory=dict)  # KV-cache groups 1..
 
 
 @dataclass
@@ -111,6 +112,16 @@ class RefBatch:
             raise BatchError("block row full")
         self._check_blocks(ids)
         r.blocks = [int(b) for b in ids]
+
+    def append_blocks_group(self, req_id: int, group: int, ids) -> None:
+        """Blocks of a further KV-cache group (a request owns one table per
+        group, [P1 §混合 KV Cache：一条请求不止一张页表]); new rows start empty."""
+        self._check_blocks(ids)
+        self.rows[self.row_of[req_id]].group_blocks.setdefault(group, []).extend(int(b) for b in ids)
+
+    def replace_blocks_group(self, req_id: int, group: int, ids) -> None:
+        self._check_blocks(ids)
+        self.rows[self.row_of[req_id]].group_blocks[group] = [int(b) for b in ids]
 
     def append_tokens(self, req_id: int, ids) -> None:
         r = self.rows[self.row_of[req_id]]

@@ -173,13 +173,41 @@ def spec_decode_metadata(query_start_loc, input_ids, num_draft_tokens):
                 bonus_logits_indices=bonus, draft_token_ids=drafts)
 
 
-def padded_block_table(rows, width: int, fill: int = -1):
-    """Rows 0..R-1 of the block table cut or padded to ``width`` entries with
-    ``fill`` past each row's own blocks (nano-vllm's prepare_block_tables pads
-    with -1 to the longest row) [P5 prepare_block_tables]."""
+def expand_kernel_blocks(manager_ids, ratio: int):
+    """A manager block of ratio * Bk tokens over a kernel of block size Bk:
+    manager id m stands for kernel ids m*ratio .. m*ratio + ratio - 1, in
+    order ([P1 §混合 KV Cache：一条请求不止一张页表])."""
     out = []
-    for r in rows:
-        out.append([int(r.blocks[j]) if j < len(r.blocks) else fill for j in range(width)])
+    for m in manager_ids:
+        for j in range(ratio):
+            out.append(int(m) * ratio + j)
+    return out
+
+
+def padded_block_table(rows, width: int, fill: int = -1, ratio: int = 1, blocks_of=None):
+    """Rows 0..R-1 of a block table (expanded to kernel blocks when ratio > 1)
+    cut or padded to ``width`` entries with ``fill`` past each row's own
+    blocks (nano-vllm's prepare_block_tables pads with -1 to the longest row)
+    [P5 prepare_block_tables].  ``blocks_of(i, row)`` picks another group's
+    block list (default: the row's own ``blocks``)."""
+    out = []
+    for i, r in enumerate(rows):
+        ids = expand_kernel_blocks(r.blocks if blocks_of is None else blocks_of(i, r), ratio)
+        out.append([ids[j] if j < len(ids) else fill for j in range(width)])
+    return out
+
+
+def group_slot_mapping(positions, req_indices, group_blocks, block_size: int, null_block: int = 0):
+    """Slots of one further KV-cache group: the same token positions through
+    that group's own block table and block size
+    ([P1 §混合 KV Cache：一条请求不止一张页表]); padded tokens (req index -1)
+    go to the group's null slot."""
+    out = []
+    for p, r in zip(positions, req_indices):
+        if r < 0:
+            out.append(null_block * block_size)
+        else:
+            out.append(int(group_blocks[r][p // block_size]) * block_size + p % block_size)
     return out
 
 

@@ -30,10 +30,15 @@ class RicError(RuntimeError):
         self.code = code
 
 
+RIC_MAX_KV_GROUPS, RIC_SLOTS_PER_TOKEN, RIC_SLOTS_NONE = 4, 0, 1
+
+
 class ric_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "max_num_reqs", "max_model_len", "block_size", "max_blocks_per_req",
-        "max_num_batched_tokens", "num_kv_blocks", "null_block", "staging_bytes")]
+        "max_num_batched_tokens", "num_kv_blocks", "null_block", "staging_bytes", "num_kv_groups")] + \
+        [(n, ctypes.c_int32 * RIC_MAX_KV_GROUPS) for n in (
+            "group_block_size", "group_num_kv_blocks", "group_slot_mode")]
 
 
 class ric_sampling(ctypes.Structure):
@@ -44,7 +49,8 @@ class ric_sampling(ctypes.Structure):
 class ric_step(ctypes.Structure):
     _fields_ = [("input_ids", _vp), ("positions", _vp), ("req_indices", _vp), ("slot_mapping", _vp),
                 ("query_start_loc", _vp), ("seq_lens", _vp), ("logits_indices", _vp), ("discard", _vp),
-                ("sample_indices", _vp), ("dev_scalars", _vp), ("cu_seqlens_k", _vp)] + \
+                ("sample_indices", _vp), ("dev_scalars", _vp), ("cu_seqlens_k", _vp),
+                ("group_slot_mapping", _vp * RIC_MAX_KV_GROUPS)] + \
                [(n, ctypes.c_int32) for n in ("num_reqs", "num_actual_tokens", "num_tokens_padded",
                                               "max_query_len", "max_seq_len", "num_sampled")]
 
@@ -84,7 +90,10 @@ def _load():
         "ric_condense": (ctypes.c_int, [_vp, _i32p]),
         "ric_flush": (ctypes.c_int, [_vp]),
         "ric_append_sampled": (ctypes.c_int, [_vp, ctypes.c_int32, _i32p, _i32p, _vp, ctypes.c_int32]),
-        "ric_block_table_padded": (ctypes.c_int, [_vp, ctypes.c_int32, ctypes.c_int32, _vp]),
+        "ric_block_table_padded": (ctypes.c_int, [_vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                  ctypes.c_int32, _vp]),
+        "ric_append_blocks_group": (ctypes.c_int, [_vp, ctypes.c_uint64, ctypes.c_int32, _i32p, ctypes.c_int32]),
+        "ric_replace_blocks_group": (ctypes.c_int, [_vp, ctypes.c_uint64, ctypes.c_int32, _i32p, ctypes.c_int32]),
         "ric_spec_decode_metadata": (ctypes.c_int, [_vp, _i32p, ctypes.POINTER(ric_spec_decode)]),
         "ric_num_reqs": (ctypes.c_int32, [_vp]),
         "ric_row_of": (ctypes.c_int32, [_vp, ctypes.c_uint64]),
@@ -130,9 +139,15 @@ def _i32(a):
 
 
 def make_config(**kw) -> ric_config:
+    """Fields by name; the per-group fields take a sequence indexed by group."""
     c = ric_config()
     for k, v in kw.items():
-        setattr(c, k, int(v))
+        if isinstance(v, (list, tuple)):
+            arr = getattr(c, k)
+            for i, x in enumerate(v):
+                arr[i] = int(x)
+        else:
+            setattr(c, k, int(v))
     return c
 
 
@@ -226,8 +241,19 @@ def ric_spec_decode_metadata(h: int, num_draft_tokens) -> ric_spec_decode:
     return out
 
 
-def ric_block_table_padded(h: int, width: int, fill: int, dst: int) -> None:
-    _err(_lib.ric_block_table_padded(_vp(h), width, fill, _vp(dst or None)))
+def ric_block_table_padded(h: int, width: int, fill: int, dst: int, group: int = 0,
+                           kernel_blocks_per_block: int = 1) -> None:
+    _err(_lib.ric_block_table_padded(_vp(h), group, kernel_blocks_per_block, width, fill, _vp(dst or None)))
+
+
+def ric_append_blocks_group(h: int, req_id: int, group: int, ids) -> None:
+    a, p = _i32(ids)
+    _err(_lib.ric_append_blocks_group(_vp(h), req_id, group, p, a.shape[0]))
+
+
+def ric_replace_blocks_group(h: int, req_id: int, group: int, ids) -> None:
+    a, p = _i32(ids)
+    _err(_lib.ric_replace_blocks_group(_vp(h), req_id, group, p, a.shape[0]))
 
 
 def ric_num_reqs(h: int) -> int:

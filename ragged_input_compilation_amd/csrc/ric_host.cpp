@@ -70,7 +70,21 @@ struct Layout {
         off_spec_logits, off_spec_target, off_spec_draft, off_spec_cu, off_spec_bonus, off_spec_d,
         off_staging, total;
     size_t staging_bytes;
+    // KV-cache groups 1..groups-1 (index g): block tables and slot outputs
+    int groups;
+    int64_t xblk_stride[kMaxGroups];
+    size_t off_xblk[kMaxGroups], off_xslot[kMaxGroups];
 };
+
+int num_groups_of(const ric_config& c) { return c.num_kv_groups <= 0 ? 1 : c.num_kv_groups; }
+int32_t group_B(const ric_config& c, int g) { return g == 0 ? c.block_size : c.group_block_size[g]; }
+int32_t group_pool(const ric_config& c, int g) {
+    return (g == 0 || c.group_num_kv_blocks[g] <= 0) ? c.num_kv_blocks : c.group_num_kv_blocks[g];
+}
+int32_t group_cap(const ric_config& c, int g) {
+    return g == 0 ? c.max_blocks_per_req : (c.max_model_len + c.group_block_size[g] - 1) / c.group_block_size[g];
+}
+bool group_slots(const ric_config& c, int g) { return g == 0 || c.group_slot_mode[g] == RIC_SLOTS_PER_TOKEN; }
 
 size_t default_staging(const ric_config& c) {
     const size_t scal_reserve = (size_t)kNumScalarCols * (size_t)c.max_num_reqs * 4 + 64 * 16;
@@ -118,6 +132,12 @@ Layout layout_of(const ric_config& c) {
     L.off_spec_cu = take((R + 1) * 4);
     L.off_spec_bonus = take(R * 4);
     L.off_spec_d = take(R * 4);
+    L.groups = num_groups_of(c);
+    for (int g = 1; g < L.groups; ++g) {
+        L.xblk_stride[g] = round4(group_cap(c, g));
+        L.off_xblk[g] = take(R * (size_t)L.xblk_stride[g] * 4);
+        L.off_xslot[g] = group_slots(c, g) ? take(NT * 4) : 0;
+    }
     L.off_staging = take(L.staging_bytes);
     L.total = o;
     return L;
@@ -134,6 +154,17 @@ int check_config(const ric_config* c) {
         return fail(RIC_EINVAL, "null_block outside [0, num_kv_blocks)");
     if ((int64_t)c->num_kv_blocks * c->block_size >= (int64_t(1) << 31))
         return fail(RIC_EINVAL, "num_kv_blocks * block_size must stay below 2^31 (int32 slots)");
+    if (c->num_kv_groups < 0 || c->num_kv_groups > kMaxGroups)
+        return fail(RIC_EINVAL, "num_kv_groups %d outside [0, %d]", c->num_kv_groups, kMaxGroups);
+    for (int g = 1; g < num_groups_of(*c); ++g) {
+        if (c->group_block_size[g] < 1) return fail(RIC_EINVAL, "group %d: block size must be positive", g);
+        if (c->group_num_kv_blocks[g] < 0) return fail(RIC_EINVAL, "group %d: negative pool size", g);
+        if (c->group_slot_mode[g] != RIC_SLOTS_PER_TOKEN && c->group_slot_mode[g] != RIC_SLOTS_NONE)
+            return fail(RIC_EINVAL, "group %d: unknown slot mode %d", g, c->group_slot_mode[g]);
+        if (c->null_block >= group_pool(*c, g)) return fail(RIC_EINVAL, "group %d: null_block outside its pool", g);
+        if ((int64_t)group_pool(*c, g) * c->group_block_size[g] >= (int64_t(1) << 31))
+            return fail(RIC_EINVAL, "group %d: pool * block size must stay below 2^31", g);
+    }
     if (c->staging_bytes < 0) return fail(RIC_EINVAL, "staging_bytes negative");
     if (c->staging_bytes > 0 && (size_t)c->staging_bytes < min_staging(*c))
         return fail(RIC_EINVAL, "staging_bytes %d below the minimum %zu (twice the scalar columns + 64 KiB)",
@@ -153,6 +184,8 @@ struct ric_batch {
 
     // device regions
     int32_t *d_tok = nullptr, *d_blk = nullptr, *d_scal = nullptr;
+    int32_t* d_xblk[kMaxGroups] = {nullptr, nullptr, nullptr, nullptr};    // groups 1..
+    int32_t* d_xslot[kMaxGroups] = {nullptr, nullptr, nullptr, nullptr};
     int32_t *d_ids = nullptr, *d_pos = nullptr, *d_req = nullptr, *d_slot = nullptr;
     int32_t *d_qsl = nullptr, *d_seq = nullptr, *d_logits = nullptr, *d_sample = nullptr;
     uint8_t* d_discard = nullptr;
@@ -204,6 +237,9 @@ struct ric_batch {
             if (live[r]) return r + 1;
         return 0;
     }
+    // block table of KV-cache group g
+    int32_t* blk(int g) const { return g == 0 ? d_blk : d_xblk[g]; }
+    int64_t bstride(int g) const { return g == 0 ? L.blk_stride : L.xblk_stride[g]; }
 };
 
 namespace {
@@ -304,10 +340,11 @@ int before_row_overwrite(ric_batch* b, int32_t row) {
     return RIC_OK;
 }
 
-int check_blocks(const ric_batch* b, const int32_t* ids, int32_t n) {
+int check_blocks(const ric_batch* b, int g, const int32_t* ids, int32_t n) {
+    const int32_t pool = group_pool(b->cfg, g);
     for (int32_t i = 0; i < n; ++i)
-        if (ids[i] < 0 || ids[i] >= b->cfg.num_kv_blocks || ids[i] == b->cfg.null_block)
-            return fail(RIC_ERANGE, "block id %d at index %d is not a usable block", ids[i], i);
+        if (ids[i] < 0 || ids[i] >= pool || ids[i] == b->cfg.null_block)
+            return fail(RIC_ERANGE, "group %d: block id %d at index %d is not a usable block", g, ids[i], i);
     return RIC_OK;
 }
 
@@ -397,6 +434,10 @@ int ric_create(const ric_config* cfg, void* stream, void* workspace, size_t work
     const Layout& L = b->L;
     b->d_tok = reinterpret_cast<int32_t*>(b->ws + L.off_tok);
     b->d_blk = reinterpret_cast<int32_t*>(b->ws + L.off_blk);
+    for (int g = 1; g < L.groups; ++g) {
+        b->d_xblk[g] = reinterpret_cast<int32_t*>(b->ws + L.off_xblk[g]);
+        if (group_slots(*cfg, g)) b->d_xslot[g] = reinterpret_cast<int32_t*>(b->ws + L.off_xslot[g]);
+    }
     b->d_scal = reinterpret_cast<int32_t*>(b->ws + L.off_scal);
     b->d_ids = reinterpret_cast<int32_t*>(b->ws + L.off_ids);
     b->d_pos = reinterpret_cast<int32_t*>(b->ws + L.off_pos);
@@ -479,7 +520,7 @@ int ric_add_request(ric_batch* b, uint64_t req_id, const int32_t* tokens, int32_
     if (num_prompt < 0 || num_prompt > num_tokens || num_computed < 0 || num_computed > num_tokens)
         return fail(RIC_ERANGE, "num_prompt %d / num_computed %d outside [0, %d]", num_prompt, num_computed, num_tokens);
     if ((num_tokens > 0 && !tokens) || (num_blocks > 0 && !blocks)) return fail(RIC_EINVAL, "payload is NULL");
-    int rc = check_blocks(b, blocks, num_blocks);
+    int rc = check_blocks(b, 0, blocks, num_blocks);
     if (rc) return rc;
     int32_t row = -1;
     for (int32_t r = 0; r < b->cfg.max_num_reqs; ++r)
@@ -495,6 +536,7 @@ int ric_add_request(ric_batch* b, uint64_t req_id, const int32_t* tokens, int32_
     rc = stage(b, b->d_blk + (int64_t)row * b->L.blk_stride, blocks, (size_t)num_blocks);
     if (rc) return rc;
     const ric_sampling sp = sampling ? *sampling : ric_sampling{1.f, 1.f, 1.f, 0};
+    // the remaining columns (block counts of groups 1..) start at zero
     const int32_t vals[kNumScalarCols] = {num_tokens, num_prompt, num_computed, 0, num_blocks, sp.top_k,
                                           as_bits(sp.temperature), as_bits(sp.top_p),
                                           as_bits(sp.repetition_penalty)};
@@ -543,37 +585,47 @@ int ric_append_tokens(ric_batch* b, uint64_t req_id, const int32_t* ids, int32_t
     return RIC_OK;
 }
 
-static int set_blocks(ric_batch* b, uint64_t req_id, const int32_t* ids, int32_t n, bool replace) {
+static int set_blocks(ric_batch* b, uint64_t req_id, int32_t g, const int32_t* ids, int32_t n, bool replace) {
     if (!b) return fail(RIC_EINVAL, "handle is NULL");
+    if (g < 0 || g >= b->L.groups) return fail(RIC_EINVAL, "group %d outside [0, %d)", g, b->L.groups);
     int32_t row;
     int rc = find(b, req_id, &row);
     if (rc) return rc;
-    const int32_t nb = replace ? 0 : b->S(kNumBlocks, row);
-    if (n < 0 || (int64_t)nb + n > b->cfg.max_blocks_per_req)
-        return fail(RIC_EFULL, "row %d: %d + %d blocks exceed max_blocks_per_req %d", row, nb, n,
-                    b->cfg.max_blocks_per_req);
+    const int col = blocks_col(g);
+    const int32_t cap = group_cap(b->cfg, g);
+    const int32_t nb = replace ? 0 : b->S(col, row);
+    if (n < 0 || (int64_t)nb + n > cap)
+        return fail(RIC_EFULL, "row %d group %d: %d + %d blocks exceed the table capacity %d", row, g, nb, n, cap);
     if (n > 0 && !ids) return fail(RIC_EINVAL, "ids is NULL");
-    rc = check_blocks(b, ids, n);
+    rc = check_blocks(b, g, ids, n);
     if (rc) return rc;
     if (replace) {
         rc = before_row_overwrite(b, row);
         if (rc) return rc;
     }
-    rc = stage(b, b->d_blk + (int64_t)row * b->L.blk_stride + nb, ids, (size_t)n);
+    rc = stage(b, b->blk(g) + (int64_t)row * b->bstride(g) + nb, ids, (size_t)n);
     if (rc) return rc;
-    b->S(kNumBlocks, row) = nb + n;
-    b->mark(kNumBlocks, row);
+    b->S(col, row) = nb + n;
+    b->mark(col, row);
     b->pending_epoch[row] = b->epoch;
     b->scheduled = false;
     return RIC_OK;
 }
 
 int ric_append_blocks(ric_batch* b, uint64_t req_id, const int32_t* ids, int32_t n) {
-    return set_blocks(b, req_id, ids, n, false);
+    return set_blocks(b, req_id, 0, ids, n, false);
 }
 
 int ric_replace_blocks(ric_batch* b, uint64_t req_id, const int32_t* ids, int32_t n) {
-    return set_blocks(b, req_id, ids, n, true);
+    return set_blocks(b, req_id, 0, ids, n, true);
+}
+
+int ric_append_blocks_group(ric_batch* b, uint64_t req_id, int32_t group, const int32_t* ids, int32_t n) {
+    return set_blocks(b, req_id, group, ids, n, false);
+}
+
+int ric_replace_blocks_group(ric_batch* b, uint64_t req_id, int32_t group, const int32_t* ids, int32_t n) {
+    return set_blocks(b, req_id, group, ids, n, true);
 }
 
 int32_t ric_condense_plan(const uint8_t* live, int32_t num_rows, int32_t* holes, int32_t* sources) {
@@ -614,10 +666,13 @@ int ric_condense(ric_batch* b, int32_t* out_num_moved) {
         MoveParams mp{};
         mp.pairs = b->d_pairs;
         mp.tokens = b->d_tok;
-        mp.blocks = b->d_blk;
+        for (int g = 0; g < b->L.groups; ++g) {
+            mp.blocks[g] = b->blk(g);
+            mp.blk_stride[g] = b->bstride(g);
+        }
+        mp.num_groups = b->L.groups;
         mp.scal = b->d_scal;
         mp.tok_stride = b->L.tok_stride;
-        mp.blk_stride = b->L.blk_stride;
         mp.max_num_reqs = MR;
         mp.num_pairs = np;
         mp.chunk_vec4 = 1024;  // 16 KiB of history per workgroup
@@ -715,22 +770,25 @@ int ric_spec_decode_metadata(ric_batch* b, const int32_t* num_draft_tokens, ric_
     return RIC_OK;
 }
 
-int ric_block_table_padded(ric_batch* b, int32_t width, int32_t fill, int32_t* dst) {
+int ric_block_table_padded(ric_batch* b, int32_t group, int32_t ratio, int32_t width, int32_t fill, int32_t* dst) {
     if (!b) return fail(RIC_EINVAL, "handle is NULL");
     if (!b->scheduled) return fail(RIC_ESTATE, "ric_schedule must follow the last row change");
-    if (width < 0 || width > b->cfg.max_blocks_per_req)
-        return fail(RIC_EINVAL, "width %d outside [0, max_blocks_per_req %d]", width, b->cfg.max_blocks_per_req);
+    if (group < 0 || group >= b->L.groups) return fail(RIC_EINVAL, "group %d outside [0, %d)", group, b->L.groups);
+    if (ratio < 1) return fail(RIC_EINVAL, "kernel_blocks_per_block %d < 1", ratio);
+    const int64_t cap = (int64_t)ratio * group_cap(b->cfg, group);
+    if (width < 0 || width > cap) return fail(RIC_EINVAL, "width %d outside [0, %lld]", width, (long long)cap);
     if (width > 0 && b->sched_R > 0 && !dst) return fail(RIC_EINVAL, "dst is NULL");
     int rc = flush(b);
     if (rc) return rc;
     PaddedTableParams p{};
-    p.blocks = b->d_blk;
-    p.num_blocks = b->dcol(kNumBlocks);
+    p.blocks = b->blk(group);
+    p.num_blocks = b->dcol(blocks_col(group));
     p.dst = dst;
-    p.blk_stride = b->L.blk_stride;
+    p.blk_stride = b->bstride(group);
     p.rows = b->sched_R;
     p.width = width;
     p.fill = fill;
+    p.ratio = ratio;
     HIP_TRY(launch_padded_table(p, b->stream));
     return RIC_OK;
 }
@@ -821,6 +879,15 @@ int ric_schedule(ric_batch* b, int32_t R, const int32_t* c, const int32_t* q) {
     int rc = check_step_rows(b->cfg, R, c, q, &b->scal[(size_t)kNumPrompt * MR], &b->scal[(size_t)kNumTokens * MR],
                              &b->scal[(size_t)kNumBlocks * MR], &N, &mq, &ms, &ns);
     if (rc) return rc;
+    // further groups with per-token slots must also cover every scheduled position
+    for (int g = 1; g < b->L.groups; ++g) {
+        if (!group_slots(b->cfg, g)) continue;
+        const int64_t B = group_B(b->cfg, g);
+        for (int32_t i = 0; i < R; ++i)
+            if (((int64_t)c[i] + q[i] + B - 1) / B > b->S(blocks_col(g), i))
+                return fail(RIC_EINVAL, "row %d group %d: %d blocks cannot hold position %lld", i, g,
+                            b->S(blocks_col(g), i), (long long)c[i] + q[i] - 1);
+    }
     for (int32_t i = 0; i < R; ++i) {
         b->S(kNumComputed, i) = c[i];
         b->S(kNumScheduled, i) = q[i];
@@ -873,6 +940,18 @@ int ric_compile(ric_batch* b, int32_t n_pad, ric_step* out) {
     p.sample_indices = b->d_sample;
     p.dev_scalars = b->d_dscal;
     p.cu_seqlens_k = b->d_cuk;
+    p.num_extra_groups = 0;
+    for (int g = 1; g < b->L.groups; ++g) {
+        if (!group_slots(b->cfg, g)) continue;
+        const int x = p.num_extra_groups++;
+        const int32_t B = group_B(b->cfg, g);
+        p.xblocks[x] = b->blk(g);
+        p.xblk_stride[x] = b->bstride(g);
+        p.xblock_size[x] = B;
+        p.xblock_shift[x] = ilog2_exact(B);
+        p.xnull_slot[x] = b->cfg.null_block * B;
+        p.xslot_mapping[x] = b->d_xslot[g];
+    }
     HIP_TRY(launch_compile(p, b->stream));
     b->compiled = true;
     if (out) {
@@ -887,6 +966,8 @@ int ric_compile(ric_batch* b, int32_t n_pad, ric_step* out) {
         out->sample_indices = b->d_sample;
         out->dev_scalars = b->d_dscal;
         out->cu_seqlens_k = b->d_cuk;
+        for (int g = 0; g < RIC_MAX_KV_GROUPS; ++g)
+            out->group_slot_mapping[g] = (g == 0) ? b->d_slot : (g < b->L.groups ? b->d_xslot[g] : nullptr);
         out->num_reqs = b->sched_R;
         out->num_actual_tokens = b->sched_N;
         out->num_tokens_padded = n_pad;

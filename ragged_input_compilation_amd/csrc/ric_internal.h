@@ -18,8 +18,14 @@ enum ScalarCol : int {
     kTemperature = 6,
     kTopP = 7,
     kRepPenalty = 8,
-    kNumScalarCols = 9
+    kNumBlocksG1 = 9,             // block counts of KV-cache groups 1..3
+    kNumBlocksG2 = 10,
+    kNumBlocksG3 = 11,
+    kNumScalarCols = 12
 };
+
+constexpr int kMaxGroups = 4;             // KV-cache groups per handle
+__host__ __device__ inline int blocks_col(int g) { return g == 0 ? kNumBlocks : kNumBlocksG1 + g - 1; }
 
 constexpr int kMaxReqsLimit = 8000;       // compile LDS: (2R + 5) int32 per workgroup < 64 KiB
 constexpr int kMaxLayersPerLaunch = 32;   // K/V pointer sets passed by value
@@ -56,6 +62,14 @@ struct CompileParams {
     int32_t* sample_indices;
     int32_t* dev_scalars;
     int32_t* cu_seqlens_k;
+    // further KV-cache groups that get per-token slots (group 0 is the one above)
+    int32_t num_extra_groups;
+    const int32_t* xblocks[kMaxGroups - 1];
+    int64_t xblk_stride[kMaxGroups - 1];
+    int32_t xblock_size[kMaxGroups - 1];
+    int32_t xblock_shift[kMaxGroups - 1];
+    int32_t xnull_slot[kMaxGroups - 1];
+    int32_t* xslot_mapping[kMaxGroups - 1];
 };
 
 struct SpecParams {
@@ -80,6 +94,7 @@ struct PaddedTableParams {
     int32_t rows;
     int32_t width;
     int32_t fill;
+    int32_t ratio;                // kernel blocks per table block (1: ids as stored)
 };
 
 struct KVParams {
@@ -113,10 +128,11 @@ struct GatherParams {
 struct MoveParams {
     const int32_t* pairs;         // [num_pairs][2] = (destination hole, source row)
     int32_t* tokens;
-    int32_t* blocks;
+    int32_t* blocks[kMaxGroups];  // per group [max_num_reqs][blk_stride[g]]
+    int64_t blk_stride[kMaxGroups];
     int32_t* scal;
     int64_t tok_stride;
-    int64_t blk_stride;
+    int32_t num_groups;
     int32_t max_num_reqs;
     int32_t num_pairs;
     int32_t chunk_vec4;           // 16-byte units of token history per workgroup

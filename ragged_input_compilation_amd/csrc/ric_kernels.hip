@@ -171,11 +171,32 @@ __global__ __launch_bounds__(kCompileThreads) void compile_kernel(CompileParams 
                     p.slot_mapping[t] = p.null_slot;
                     atomicAdd(p.dev_scalars + 6, 1);
                 }
+                // Further KV-cache groups: the same position through each
+                // group's own block table and block size ([P1 §混合 KV Cache：
+                // 一条请求不止一张页表]).
+                for (int x = 0; x < p.num_extra_groups; ++x) {
+                    const int B = p.xblock_size[x];
+                    int xlb, xoff;
+                    if (p.xblock_shift[x] >= 0) {
+                        xlb = pos >> p.xblock_shift[x];
+                        xoff = pos & (B - 1);
+                    } else {
+                        xlb = pos / B;
+                        xoff = pos - xlb * B;
+                    }
+                    if (pos >= 0 && xlb < p.xblk_stride[x]) {
+                        p.xslot_mapping[x][t] = p.xblocks[x][(int64_t)r * p.xblk_stride[x] + xlb] * B + xoff;
+                    } else {
+                        p.xslot_mapping[x][t] = p.xnull_slot[x];
+                        atomicAdd(p.dev_scalars + 6, 1);
+                    }
+                }
             } else {
                 p.input_ids[t] = 0;
                 p.positions[t] = 0;
                 p.req_indices[t] = -1;
                 p.slot_mapping[t] = p.null_slot;
+                for (int x = 0; x < p.num_extra_groups; ++x) p.xslot_mapping[x][t] = p.xnull_slot[x];
             }
         }
         return;
@@ -423,10 +444,12 @@ __global__ __launch_bounds__(256) void move_rows_kernel(MoveParams p) {
     u32x4* td = reinterpret_cast<u32x4*>(p.tokens + (int64_t)dst_row * p.tok_stride);
     for (int v = v0 + threadIdx.x; v < v1; v += 256) td[v] = ts[v];
     if (blockIdx.x == 0) {
-        const int nb = min(p.scal[(int64_t)kNumBlocks * p.max_num_reqs + src_row], (int)p.blk_stride);
-        const u32x4* bs = reinterpret_cast<const u32x4*>(p.blocks + (int64_t)src_row * p.blk_stride);
-        u32x4* bd = reinterpret_cast<u32x4*>(p.blocks + (int64_t)dst_row * p.blk_stride);
-        for (int v = threadIdx.x; v < ((nb + 3) >> 2); v += 256) bd[v] = bs[v];
+        for (int g = 0; g < p.num_groups; ++g) {
+            const int nb = min(p.scal[(int64_t)blocks_col(g) * p.max_num_reqs + src_row], (int)p.blk_stride[g]);
+            const u32x4* bs = reinterpret_cast<const u32x4*>(p.blocks[g] + (int64_t)src_row * p.blk_stride[g]);
+            u32x4* bd = reinterpret_cast<u32x4*>(p.blocks[g] + (int64_t)dst_row * p.blk_stride[g]);
+            for (int v = threadIdx.x; v < ((nb + 3) >> 2); v += 256) bd[v] = bs[v];
+        }
         if (threadIdx.x < kNumScalarCols) {
             const int64_t col = (int64_t)threadIdx.x * p.max_num_reqs;
             p.scal[col + dst_row] = p.scal[col + src_row];
@@ -534,7 +557,11 @@ __global__ __launch_bounds__(256) void padded_table_kernel(PaddedTableParams p) 
     const int j = blockIdx.x * 256 + threadIdx.x;
     if (j >= p.width) return;
     const int nb = min((int64_t)p.num_blocks[r], p.blk_stride);
-    p.dst[(int64_t)r * p.width + j] = (j < nb) ? p.blocks[(int64_t)r * p.blk_stride + j] : p.fill;
+    // ratio > 1: each stored (manager) block id m stands for kernel blocks
+    // m*ratio .. m*ratio + ratio-1 ([P1 §混合 KV Cache], map_to_kernel_blocks)
+    const int b = j / p.ratio;
+    p.dst[(int64_t)r * p.width + j] =
+        (b < nb) ? p.blocks[(int64_t)r * p.blk_stride + b] * p.ratio + (j - b * p.ratio) : p.fill;
 }
 
 hipError_t launch_padded_table(const PaddedTableParams& p, hipStream_t s) {

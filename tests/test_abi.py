@@ -145,6 +145,21 @@ def test_config_validation(ric):
         assert ric.ric_workspace_bytes(ric.make_config(**{**base, **bad})) == 0
 
 
+def test_group_config_validation(ric):
+    good = dict(max_num_reqs=4, max_model_len=64, block_size=16, max_blocks_per_req=4, max_num_batched_tokens=8,
+                num_kv_blocks=10, null_block=0, staging_bytes=0, num_kv_groups=2, group_block_size=[0, 8],
+                group_num_kv_blocks=[0, 0], group_slot_mode=[0, 0])
+    one = ric.ric_workspace_bytes(ric.make_config(**{**good, "num_kv_groups": 1}))
+    two = ric.ric_workspace_bytes(ric.make_config(**good))
+    # a second group adds a [4][8] block table and a slot output of 8 entries
+    assert two > one > 0
+    assert ric.ric_workspace_bytes(ric.make_config(**{**good, "group_slot_mode": [0, 1]})) < two
+    for bad in (dict(num_kv_groups=5), dict(num_kv_groups=-1), dict(group_block_size=[0, 0]),
+                dict(group_slot_mode=[0, 7]), dict(group_num_kv_blocks=[0, -1]),
+                dict(group_block_size=[0, 1 << 20], group_num_kv_blocks=[0, 1 << 12])):
+        assert ric.ric_workspace_bytes(ric.make_config(**{**good, **bad})) == 0
+
+
 @pytest.mark.parametrize("name", workloads.CONFIG_NAMES)
 def test_workspace_fits(ric, name):
     w = workloads.get(name)

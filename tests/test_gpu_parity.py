@@ -472,7 +472,7 @@ def test_minimum_staging_forces_chunked_uploads(rt):
     req = workloads.Req(0, tokens, T, c0, q, blocks)
     w = _simple_rows_workload([req], B, 2, M, 40001)
     cfg = runner.config_of(w)
-    cfg.staging_bytes = 2 * 9 * 2 * 4 + (64 << 10)
+    cfg.staging_bytes = 96 * cfg.max_num_reqs + (64 << 10)     # the documented minimum
     b = runner.Batch(cfg)
     b.load_history(w)
     ref, order = replay_history(w)

@@ -196,6 +196,43 @@ def test_append_sampled_then_decode():
     assert out["positions"] == [t - 1 for t in T]
 
 
+def test_kernel_block_expansion_pin():
+    g = golden("p1_kernel_blocks.json")
+    ratio = g["manager_block_size"] // g["kernel_block_size"]
+    assert step.expand_kernel_blocks(g["manager_ids"], ratio) == g["expect"]["kernel_ids"]
+
+
+def test_kernel_blocks_give_the_same_slots():
+    """Slots through manager blocks of size k*Bk equal slots through the
+    expanded kernel blocks of size Bk, for every position: the expansion
+    changes the table an attention kernel reads, not where K/V lands."""
+    rng = np.random.default_rng(51)
+    for trial in range(200):
+        Bk = int(rng.integers(1, 9))
+        k = int(rng.integers(1, 5))
+        ids = rng.permutation(np.arange(1, 64))[:int(rng.integers(1, 8))]
+        kern = step.expand_kernel_blocks(ids, k)
+        for p in range(len(ids) * k * Bk):
+            via_manager = int(ids[p // (k * Bk)]) * (k * Bk) + p % (k * Bk)
+            via_kernel = kern[p // Bk] * Bk + p % Bk
+            assert via_manager == via_kernel
+
+
+def test_group_slot_mapping_matches_compile_for_one_group():
+    """With a single group, the per-group slot routine reproduces the
+    compile's slot_mapping, padding included."""
+    rng = np.random.default_rng(52)
+    for trial in range(50):
+        B = int(rng.integers(1, 9))
+        rows = rows_of(workloads.random_batch(rng, num_reqs=4, block_size=B, max_model_len=200,
+                                              num_kv_blocks=400, max_q=9, max_c=40))
+        n_pad = sum(r.num_scheduled for r in rows) + 3
+        out = step.compile_step(rows, block_size=B, max_num_reqs=4, max_model_len=200, max_num_batched_tokens=n_pad,
+                                num_kv_blocks=400, n_pad=n_pad)
+        got = step.group_slot_mapping(out["positions"], out["req_indices"], [r.blocks for r in rows], B)
+        assert got == out["slot_mapping"]
+
+
 def test_spec_decode_reduces_to_plain_logits_without_drafts():
     """No drafts: one logits row per request, at query_start_loc[1:] - 1 (the
     closed form the second page prints for [0,2,9,12] -> [1,8,11])."""
