@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 KV_EVENT_EVERY = 4      # timed steps carrying events around the K/V launch: 1 in 4
+KV_LONG_RUN_TOKENS = 64  # mean scheduled tokens per request from which the K/V hint is set
 METRIC = "scheduled tokens/sec per step (compile + KV write); achieved HBM GB/s vs peak"
 DESCRIPTIONS = {
     "worked_example": "3 requests (prefill 7, decode 5+1, chunk 10..21), N=20 padded to 32, block 16, "
@@ -126,9 +127,11 @@ class GpuStep:
         st = ctypes.c_void_p(self.stream or None)
         lib = ric.lib()
         self.lib = lib
+        # the caller knows its step's shape: long prefill chunks write long runs of consecutive slots
+        self.kv_flags = ric.RIC_KV_LONG_RUNS if self.N >= KV_LONG_RUN_TOKENS * max(len(live), 1) else 0
         self.kv_args = [ctypes.cast(a, pp) for a in self._ptrs] + [
             L, ctypes.c_void_p(self.step.slot_mapping), self.n_pad, 0, w.row_bytes,
-            w.num_kv_blocks * w.block_size, None, st]
+            w.num_kv_blocks * w.block_size, None, self.kv_flags, st]
         row = w.hidden_size * 2
         if w.gather == "all":
             idx, cnt, rows = self.step.logits_indices, None, len(live)
@@ -402,7 +405,8 @@ def main():
                    "num_tokens": N, "num_layers": w0.num_layers, "rotation_instances": S},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": load_traffic(kv_kernel_name(w0, sb["N"]), args.config),
-                     "kernel": kv_kernel_name(w0, sb["N"]), "bytes_per_launch": sb["kv"],
+                     "kernel": kv_kernel_name(w0, sb["N"]), "kv_flags": sets[0].kv_flags,
+                     "bytes_per_launch": sb["kv"],
                      "avg_launch_us": kv_mean * 1e3, "event_samples": len(ev)},
         "step_bytes": sb["total"],
         "step_gbps": sb["total"] / (ms_per_step * 1e-3) / 1e9,

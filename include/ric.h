@@ -318,12 +318,19 @@ int ric_compile(ric_batch* b, int32_t num_tokens_padded, ric_step* out);
  *                     src_row_stride and every pointer 16-byte aligned
  *   dev_status        optional DEVICE int32: incremented once per row whose
  *                     slot is outside [0, num_slots) (that row is not written)
- * All layers are written by one launch.  Errors: EINVAL (alignment, counts),
- * EHIP. */
+ *   flags             0, or RIC_KV_LONG_RUNS: a performance hint that most
+ *                     consecutive tokens go to consecutive slots (prefill
+ *                     chunks; e.g. num_actual_tokens / num_reqs >= 64).  It
+ *                     selects streaming loads, measured ~4% faster on long
+ *                     runs and ~20% slower on scattered decode slots; results
+ *                     are identical either way.
+ * All layers are written by one launch.  Errors: EINVAL (alignment, counts,
+ * unknown flags), EHIP. */
+#define RIC_KV_LONG_RUNS 1u
 int ric_reshape_and_cache(const void* const* k, const void* const* v, void* const* k_cache,
                           void* const* v_cache, int32_t num_layers, const int32_t* slot_mapping,
                           int32_t num_tokens, int64_t src_row_stride, int32_t row_bytes,
-                          int64_t num_slots, int32_t* dev_status, void* stream);
+                          int64_t num_slots, int32_t* dev_status, uint32_t flags, void* stream);
 
 /* Gather rows: dst[m] = src[idx[m]] for m < count, where count = *dev_count
  * (DEVICE int32, e.g. ric_step.dev_scalars + 5 for the compacted list) or

@@ -31,6 +31,7 @@ class RicError(RuntimeError):
 
 
 RIC_MAX_KV_GROUPS, RIC_SLOTS_PER_TOKEN, RIC_SLOTS_NONE = 4, 0, 1
+RIC_KV_LONG_RUNS = 1
 
 
 class ric_config(ctypes.Structure):
@@ -104,7 +105,8 @@ def _load():
         "ric_schedule": (ctypes.c_int, [_vp, ctypes.c_int32, _i32p, _i32p]),
         "ric_compile": (ctypes.c_int, [_vp, ctypes.c_int32, ctypes.POINTER(ric_step)]),
         "ric_reshape_and_cache": (ctypes.c_int, [ctypes.POINTER(_vp)] * 4 + [
-            ctypes.c_int32, _vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int64, _vp, _vp]),
+            ctypes.c_int32, _vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int64, _vp,
+            ctypes.c_uint32, _vp]),
         "ric_gather_rows": (ctypes.c_int, [_vp, ctypes.c_int64, ctypes.c_int64, _vp, _vp, ctypes.c_int32,
                                            ctypes.c_int32, _vp, ctypes.c_int64, _vp, _vp]),
         "ric_padded_size": (ctypes.c_int32, [_i32p, ctypes.c_int32, ctypes.c_int32]),
@@ -311,14 +313,14 @@ def ric_compile(h: int, num_tokens_padded: int) -> ric_step:
 
 def ric_reshape_and_cache(k_ptrs, v_ptrs, k_cache_ptrs, v_cache_ptrs, slot_mapping: int, num_tokens: int,
                           row_bytes: int, num_slots: int, src_row_stride: int = 0, dev_status: int = 0,
-                          stream: int = 0) -> None:
+                          flags: int = 0, stream: int = 0) -> None:
     L = len(k_ptrs)
     if not (len(v_ptrs) == len(k_cache_ptrs) == len(v_cache_ptrs) == L):
         raise ValueError("pointer lists differ in length")
     arr = [(_vp * max(L, 1))(*[_vp(p) for p in lst]) for lst in (k_ptrs, v_ptrs, k_cache_ptrs, v_cache_ptrs)]
     _err(_lib.ric_reshape_and_cache(*[ctypes.cast(a, ctypes.POINTER(_vp)) for a in arr], L,
                                     _vp(slot_mapping), num_tokens, src_row_stride, row_bytes, num_slots,
-                                    _vp(dev_status or None), _vp(stream or None)))
+                                    _vp(dev_status or None), flags, _vp(stream or None)))
 
 
 def ric_gather_rows(src: int, src_row_stride: int, src_rows: int, idx: int, dev_count: int, max_rows: int,

@@ -983,8 +983,9 @@ static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 int ric_reshape_and_cache(const void* const* k, const void* const* v, void* const* k_cache, void* const* v_cache,
                           int32_t num_layers, const int32_t* slot_mapping, int32_t num_tokens,
                           int64_t src_row_stride, int32_t row_bytes, int64_t num_slots, int32_t* dev_status,
-                          void* stream) {
+                          uint32_t flags, void* stream) {
     if (num_layers < 0 || num_tokens < 0) return fail(RIC_EINVAL, "negative count");
+    if (flags & ~RIC_KV_LONG_RUNS) return fail(RIC_EINVAL, "unknown flags 0x%x", flags);
     if (num_layers == 0 || num_tokens == 0) return RIC_OK;
     if (!k || !v || !k_cache || !v_cache || !slot_mapping) return fail(RIC_EINVAL, "NULL pointer argument");
     if (row_bytes <= 0 || row_bytes % 16 != 0) return fail(RIC_EINVAL, "row_bytes %d not a positive multiple of 16", row_bytes);
@@ -1000,6 +1001,7 @@ int ric_reshape_and_cache(const void* const* k, const void* const* v, void* cons
     p.slot = slot_mapping;
     p.src_stride = src_row_stride;
     p.num_slots = num_slots;
+    p.long_runs = (flags & RIC_KV_LONG_RUNS) ? 1 : 0;
     p.status = dev_status;
     p.num_tokens = num_tokens;
     p.row_bytes = row_bytes;

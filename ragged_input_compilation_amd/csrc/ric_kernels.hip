@@ -380,7 +380,10 @@ hipError_t launch_kv_scatter(const KVParams& p_in, int num_layers, hipStream_t s
     }
     p.rows_per_wg = p.rows_per_wg > 0 ? p.rows_per_wg : max(1, kKvTileBytes / p.row_bytes);
     const int gx = (p.num_tokens + p.rows_per_wg - 1) / p.rows_per_wg;
-    hipLaunchKernelGGL((kv_chunk_kernel<1, false, true>), dim3(gx, 2 * num_layers), dim3(256), 0, s, p);
+    if (p.long_runs)
+        hipLaunchKernelGGL((kv_chunk_kernel<1, true, true>), dim3(gx, 2 * num_layers), dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL((kv_chunk_kernel<1, false, true>), dim3(gx, 2 * num_layers), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

@@ -177,12 +177,13 @@ def alloc_sources(w, n_tokens: int, seed: int, num_layers: Optional[int] = None,
 
 
 def reshape_and_cache(kv: KVSet, slot_mapping: int, num_tokens: int, dev_status: int = 0,
-                      stream: Optional[int] = None) -> None:
+                      stream: Optional[int] = None, flags: int = 0) -> None:
     ric.ric_reshape_and_cache([t.data_ptr() for t in kv.k], [t.data_ptr() for t in kv.v],
                               [t.data_ptr() for t in kv.kc], [t.data_ptr() for t in kv.vc],
                               slot_mapping, num_tokens, kv.row_bytes, kv.num_slots,
                               src_row_stride=kv.k[0].stride(0) * kv.k[0].element_size(),
-                              dev_status=dev_status, stream=current_stream() if stream is None else stream)
+                              dev_status=dev_status, flags=flags,
+                              stream=current_stream() if stream is None else stream)
 
 
 def gather(hidden: torch.Tensor, idx_ptr: int, dev_count_ptr: int, max_rows: int, out: torch.Tensor,

@@ -136,12 +136,13 @@ def test_kv_write_worked_example_full(rt):
     b.close()
 
 
-@pytest.mark.parametrize("name", ["decode_heavy", "mixed", "churn", "long_context"])
-def test_kv_write_full_size_sampled(rt, name):
+@pytest.mark.parametrize("name,flags", [("decode_heavy", 0), ("mixed", 0), ("churn", 0), ("long_context", 0),
+                                        ("decode_heavy", 1), ("long_context", 1)])
+def test_kv_write_full_size_sampled(rt, name, flags):
     """Full-size caches, every layer of the configuration, one launch: sampled
     real tokens (plus every token of up to 2048) are compared with their source
     rows at the oracle's slot, and sampled slots outside the step keep their
-    sentinel."""
+    sentinel.  The long-runs hint (flags 1) changes only how rows are loaded."""
     ric, runner = rt
     w = workloads.get(name)
     b, s, ref, order, exp, _ = _compile(rt, w)
@@ -150,7 +151,7 @@ def test_kv_write_full_size_sampled(rt, name):
     k, v = runner.alloc_sources(w, n_pad, seed=w.seed + 17)
     kv = runner.KVSet(k, v, kc, vc, w.row_bytes, w.num_kv_blocks * w.block_size)
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    runner.reshape_and_cache(kv, s.slot_mapping, n_pad, dev_status=status.data_ptr())
+    runner.reshape_and_cache(kv, s.slot_mapping, n_pad, dev_status=status.data_ptr(), flags=flags)
     torch.cuda.synchronize()
     assert int(status.item()) == 0
     rng = np.random.default_rng(5)
@@ -404,6 +405,11 @@ def test_out_of_range_indices_are_reported_not_written(rt):
     assert int(status.item()) == 4
     assert torch.equal(kc1[3], k1[0]) and torch.equal(vc1[7], v1[3])
     assert bool((kc1[others] == -1).all()) and bool((vc1[others] == -1).all())
+    # an unknown hint bit is rejected before anything is launched
+    with pytest.raises(ric.RicError) as e:
+        ric.ric_reshape_and_cache([k.data_ptr()], [v.data_ptr()], [kc.data_ptr()], [vc.data_ptr()],
+                                  slot.data_ptr(), 4, row_bytes, nslots, flags=2, stream=runner.current_stream())
+    assert e.value.code == ric.RIC_EINVAL
     src = torch.arange(5 * 16, dtype=torch.int32, device="cuda").reshape(5, 16)
     idx = torch.tensor([4, 5, -1, 0], dtype=torch.int32, device="cuda")
     out = torch.full((4, 16), 9, dtype=torch.int32, device="cuda")
