@@ -19,6 +19,7 @@ import json
 import math
 import mmap
 import os
+import re
 import sys
 import time
 
@@ -85,21 +86,28 @@ def kv_kernel_name(w, n_tokens):
     return "kv_chunk_kernel"
 
 
+def code_digest(text):
+    """sha256 of C++ source with comments and whitespace removed, so that a
+    comment edit keeps counter readings valid and any code edit voids them."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()
+
+
 def kernel_source_digest():
-    with open(os.path.join(ROOT, "ragged_input_compilation_amd", "csrc", "ric_kernels.hip"), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    with open(os.path.join(ROOT, "ragged_input_compilation_amd", "csrc", "ric_kernels.hip"), encoding="utf-8") as f:
+        return code_digest(f.read())
 
 
 def load_traffic(kernel_name, workload_name):
     """HBM bytes per launch of the K/V kernel from the committed counter runs
     (profiles/<kernel>_<workload>_pmc.md), or None when there are none or they
     were taken on another version of the kernel source."""
-    import re
     path = os.path.join(ROOT, "profiles", f"{kernel_name}_{workload_name}_pmc.md")
     if not os.path.exists(path):
         return None
     text = open(path, encoding="utf-8").read()
-    digest = re.search(r"^kernel_source_sha256: ([0-9a-f]{64})$", text, re.M)
+    digest = re.search(r"^kernel_code_sha256: ([0-9a-f]{64})$", text, re.M)
     traffic = re.search(r"^traffic_bytes_per_launch: (\d+)$", text, re.M)
     if not digest or not traffic or digest.group(1) != kernel_source_digest():
         return None
@@ -274,8 +282,10 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU: this step needs no exchange between GPUs and every box here has "
-              f"one GPU (asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        print(f"bench.py measures one GPU (asked for --gpus {args.gpus}, WORLD_SIZE {world}): the step needs no "
+              f"exchange between GPUs; under data parallelism each GPU compiles its own batch, under tensor "
+              f"parallelism each runs the same compile and writes its own K/V heads, so the per-GPU figure is "
+              f"the one to measure.", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

@@ -15,7 +15,7 @@ request batch:
   every column of the row together ([P1 §行号是一种短生命周期地址];
   [P1 §为什么删除后还要压紧]).
 
-Reading (DESIGN.md): a new request takes the lowest free row; condense pairs
+Reading: a new request takes the lowest free row; condense pairs
 the k-th lowest hole with the k-th highest live row while the hole lies below
 that row, which reproduces the A,B,C,D -> A,D,C example of the first page.
 """

@@ -22,7 +22,7 @@ token at a time, written so each line can be checked against the pages:
 * the t-th new K/V row is written to slot_mapping[t] with no request id
   involved ([P1 §3. 物理 KV 槽位]; [P3 §实现]).
 
-Readings where the pages leave a value open (also listed in the design doc):
+Readings where the pages leave a value open:
 
 * pad token t in [N, N_pad): input_id 0, position 0, req_index -1,
   slot null_block * B.

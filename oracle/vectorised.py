@@ -14,7 +14,7 @@ oracle that the per-token loops in ``step`` must agree with:
   ([P2 §8.3.2 slot_mapping：新 token 写到哪个 KV 槽]);
 * ``logits_indices = query_start_loc[1:] - 1`` ([P2 §8.6.3]).
 
-Pad readings are the same as in ``step`` (listed in the design doc).
+Pad readings are the same as in ``step``.
 """
 from __future__ import annotations
 

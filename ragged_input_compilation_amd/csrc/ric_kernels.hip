@@ -9,9 +9,8 @@
 // Nothing here is a contraction, so no MFMA: the compile is a few integer
 // operations per token behind two dependent loads, and the K/V write and the
 // gather are indexed copies bound by HBM bandwidth.  The copies move 16-byte
-// vectors per lane with non-temporal loads and stores (each byte is touched
-// once per step), keep several loads in flight per lane before storing, and
-// use 64-bit byte offsets.
+// vectors per lane, use non-temporal accesses where a byte is touched once per
+// step and the measurements favour them, and compute byte offsets in 64 bits.
 #include "ric_internal.h"
 
 namespace ric {
@@ -251,12 +250,16 @@ hipError_t launch_compile(const CompileParams& p, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // Paged K/V write: row t of every K and V source goes to cache row slot[t]
 // ([P1 §3. 物理 KV 槽位]; [P3 §实现]).  Two launch shapes, chosen by size from
-// a measured sweep on MI355X (the design doc lists the numbers):
+// measured sweeps on MI355X:
 //
 // * chunk tiles (large launches): blockIdx.y = 2*layer + (K:0, V:1),
 //   blockIdx.x = a run of rows of about 4 KiB; lanes walk the run's 16-byte
 //   chunks in order, so a source run is read contiguously and each cache row
-//   is written contiguously.  Plain loads, non-temporal stores.
+//   is written contiguously.  Non-temporal stores; loads are plain, or
+//   non-temporal when the caller reports long runs of consecutive slots
+//   (streaming loads gain ~4% there and lose ~20% on scattered decode slots).
+//   More bytes in flight per lane (2-4 loads before the stores, bigger tiles,
+//   a persistent grid) measured slower at every size here.
 // * wave rows (few tokens, many layers): blockIdx.y = layer; each wave owns
 //   ROWS consecutive tokens and copies both the K and the V row of each, so
 //   one wave-uniform (scalar) slot load serves both; 4*ROWS*CPL 16-byte loads

@@ -1,0 +1,60 @@
+"""Host-side pieces of bench.py, on the CPU: the algorithmic byte count of a
+step, the counter-file lookup and its code digest, and the refusal of more
+than one GPU."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_step_bytes_long_context():
+    """4 x 8192 tokens of 2 KiB K and V rows, one layer: read 2*N*row + 4N,
+    write 2*N*row."""
+    sb = bench.step_bytes(workloads.get("long_context"))
+    N, row = 32768, 2048
+    assert (sb["R"], sb["N"]) == (4, N)
+    assert sb["kv"] == 2 * N * row + 4 * N + 2 * N * row == 268566528
+
+
+def test_step_bytes_decode_heavy():
+    sb = bench.step_bytes(workloads.get("decode_heavy"))
+    assert sb["kv"] == 32 * (4 * 256 * 2048 + 4 * 256) == 67141632
+    assert sb["gather_rows"] == 256
+
+
+def test_code_digest_ignores_comments_only():
+    code = "int f(int x) {\n  return x + 1;  // one more\n}\n/* block\n comment */\n"
+    same = "// header\nint f(int x) {   return x + 1;\n}\n"
+    other = "int f(int x) {\n  return x + 2;\n}\n"
+    assert bench.code_digest(code) == bench.code_digest(same)
+    assert bench.code_digest(code) != bench.code_digest(other)
+
+
+def test_load_traffic_needs_matching_code(tmp_path, monkeypatch):
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    (prof / "kv_chunk_kernel_x_pmc.md").write_text(
+        "traffic_bytes_per_launch: 123\nkernel_code_sha256: " + "0" * 64 + "\n")
+    (prof / "kv_chunk_kernel_y_pmc.md").write_text(
+        "traffic_bytes_per_launch: 456\nkernel_code_sha256: " + bench.kernel_source_digest() + "\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_digest", lambda: bench.code_digest("x"))
+    assert bench.load_traffic("kv_chunk_kernel", "x") is None
+    assert bench.load_traffic("kv_chunk_kernel", "missing") is None
+    (prof / "kv_chunk_kernel_z_pmc.md").write_text(
+        "traffic_bytes_per_launch: 789\nkernel_code_sha256: " + bench.code_digest("x") + "\n")
+    assert bench.load_traffic("kv_chunk_kernel", "z") == 789
+
+
+@pytest.mark.parametrize("gpus", [2, 8])
+def test_more_than_one_gpu_is_refused(gpus):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", str(gpus)],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
