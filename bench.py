@@ -27,7 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-KV_EVENT_EVERY = 4      # timed steps carrying events around the K/V launch: 1 in 4
+KV_EVENT_EVERY = 8      # timed steps carrying events around the K/V launch: 1 in 8 (each pair perturbs its step)
 KV_LONG_RUN_TOKENS = 64  # mean scheduled tokens per request from which the K/V hint is set
 METRIC = "scheduled tokens/sec per step (compile + KV write); achieved HBM GB/s vs peak"
 DESCRIPTIONS = {
@@ -313,9 +313,15 @@ def main():
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 
-    def run(n, mode):
+    def event_pairs(n):
+        return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range((n + KV_EVENT_EVERY - 1) // KV_EVENT_EVERY)]
+
+    def run(n, mode, pool=None):
         """mode "none": no events; "kv": events around the K/V launch only (the
-        timed region); "all": events around each of the three kernels."""
+        timed region; `pool` holds the events, created beforehand since
+        creating them costs host time); "all": events around each of the three
+        kernels."""
         ev = []
         for i in range(n):
             st = sets[i % S]
@@ -328,7 +334,7 @@ def main():
                 st.kv()
                 st.gather()
             elif mode == "kv":
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a, b = pool[i // KV_EVENT_EVERY]
                 st.compile()
                 a.record()
                 st.kv()
@@ -344,9 +350,10 @@ def main():
         return ev
 
     run(args.warmup, "none")
+    pool = event_pairs(args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev = run(args.steps, "kv")
+    ev = run(args.steps, "kv", pool)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
@@ -358,6 +365,7 @@ def main():
     torch.cuda.synchronize()
     t2 = time.perf_counter()
     run(args.steps, "none")
+    host_ms = (time.perf_counter() - t2) * 1e3 / args.steps     # enqueue only: the launches are asynchronous
     torch.cuda.synchronize()
     ms_no_events = (time.perf_counter() - t2) * 1e3 / args.steps
     evs = run(min(args.steps, 100), "all")
@@ -422,6 +430,7 @@ def main():
         "step_gbps": sb["total"] / (ms_per_step * 1e-3) / 1e9,
         "step_frac_of_peak": sb["total"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "ms_per_step_without_events": ms_no_events,
+        "host_enqueue_us_per_step": host_ms * 1e3,
         "kernels_us": {"compile": mean(comp_ms) * 1e3, "kv_scatter": kv_mean * 1e3,
                        "gather": mean(ga_ms) * 1e3, "kv_scatter_after_cache_flush": kv_cold_ms * 1e3},
         "pcie_inclusive_tokens_per_s": N / (pcie_ms * 1e-3),
