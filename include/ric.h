@@ -160,8 +160,8 @@ int ric_create(const ric_config* cfg, void* stream, void* workspace, size_t work
  * handle is accepted. */
 int ric_destroy(ric_batch* b);
 
-/* Change the stream later calls enqueue on (ordering with earlier work is the
- * caller's business). */
+/* Change the stream later calls enqueue on.  Waits first for the work already
+ * enqueued on the previous stream, so nothing later can overtake it. */
 int ric_set_stream(ric_batch* b, void* stream);
 
 /* Message of the last failed call on this thread ("" if none). */
