@@ -120,7 +120,9 @@ class GpuStep:
     def __init__(self, ric, runner, torch, w, kc, vc, hidden, out, seed):
         self.w = w
         self.batch = runner.Batch(runner.config_of(w))
-        self.batch.load_history(w)
+        self.condense = self._history_with_timed_condense(ric, torch, w) if w.finished else None
+        if not w.finished:
+            self.batch.load_history(w)
         self.batch.schedule_from(w)
         live = w.live_requests()
         self.N = sum(r.num_scheduled for r in live)
@@ -154,6 +156,33 @@ class GpuStep:
     def _check(self, rc):
         if rc != 0:
             raise RuntimeError(self.ric.ric_last_error())
+
+    def _history_with_timed_condense(self, ric, torch, w):
+        """The workload's history (adds, removals, condense, refills) with HIP
+        events around the condense alone; returns its time, the rows it moved
+        and their algorithmic bytes (each moved row reads and writes its token
+        history, its block row and the 12 scalar columns)."""
+        h = self.batch.h
+        for r in w.initial:
+            self.batch.add(r)
+        for rid in w.finished:
+            ric.ric_remove_request(h, rid)
+        ric.ric_flush(h)
+        by_row = [ric.ric_req_at(h, row) for row in range(w.max_num_reqs)]
+        plan = ric.ric_condense_plan([x is not None for x in by_row])
+        by_id = w.by_id()
+        nbytes = sum(2 * (4 * len(by_id[by_row[src]].tokens) + 4 * len(by_id[by_row[src]].blocks) + 4 * 12)
+                     for _, src in plan)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        moved = ric.ric_condense(h)
+        b.record()
+        for r in w.refill:
+            self.batch.add(r)
+        ric.ric_flush(h)
+        torch.cuda.synchronize()
+        return dict(us=a.elapsed_time(b) * 1e3, rows_moved=moved, bytes=nbytes)
 
     def compile(self):
         self._check(self.lib.ric_compile(self.h, self.n_pad, ctypes.byref(self.step_out)))
@@ -252,9 +281,56 @@ def cpu_baseline(w, seconds):
     for m in maps:
         m.close()
     return dict(value=N * reps / el, unit="tokens/s", cores=1, kind="oracle",
+                host_cpu_count=os.cpu_count(), host_cpus_allowed=len(os.sched_getaffinity(0)),
                 sample=f"{reps} full steps of the same configuration (seed instance 0) in {el:.1f} s; "
                        f"single-thread C oracle (nano-vllm block-range compile, memcpy K/V scatter into "
                        f"mmap'd full-size host caches, hidden-row gather)")
+
+
+def copy_ceiling(ric, torch, sets, w, sb, reps=20):
+    """What a plain copy of the K/V launch's bytes reaches on this GPU: torch's
+    own device copy (half the bytes read, half written, rotating over buffers
+    that together exceed 1 GiB), and the library's K/V launch with identity
+    slots (each source row to consecutive cache rows)."""
+    half = sb["kv"] // 2
+    pairs = max(2, min(16, -(-(1 << 30) // (2 * half))))
+    bufs = [(torch.empty(half, dtype=torch.uint8, device="cuda"), torch.empty(half, dtype=torch.uint8, device="cuda"))
+            for _ in range(pairs)]
+    for src, _ in bufs:
+        src.fill_(1)
+    times = []
+    for i in range(reps + 2):
+        src, dst = bufs[i % pairs]
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        times.append((a, b))
+    torch.cuda.synchronize()
+    t_torch = sorted(a.elapsed_time(b) for a, b in times[2:])[reps // 2]
+    del bufs
+
+    B, n_pad = w.block_size, sets[0].n_pad
+    num_slots = w.num_kv_blocks * B
+    slots = []
+    for k, st in enumerate(sets):
+        off = B + k * n_pad if B + (len(sets) + 1) * n_pad <= num_slots else B
+        slots.append(torch.arange(off, off + n_pad, dtype=torch.int32, device="cuda"))
+    times = []
+    for i in range(reps + 2):
+        k = i % len(sets)
+        args = list(sets[k].kv_args)
+        args[5] = ctypes.c_void_p(slots[k].data_ptr())
+        args[11] = ric.RIC_KV_LONG_RUNS
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        sets[k]._check(sets[k].lib.ric_reshape_and_cache(*args))
+        b.record()
+        times.append((a, b))
+    torch.cuda.synchronize()
+    t_ident = sorted(a.elapsed_time(b) for a, b in times[2:])[reps // 2]
+    return dict(bytes=sb["kv"], torch_copy_us=t_torch * 1e3, torch_copy_gbps=2 * half / (t_torch * 1e-3) / 1e9,
+                identity_slots_us=t_ident * 1e3, identity_slots_gbps=sb["kv"] / (t_ident * 1e-3) / 1e9)
 
 
 def calibrate_copy(ric, torch, stream):
@@ -387,20 +463,35 @@ def main():
     torch.cuda.synchronize()
     pcie_ms = (time.perf_counter() - t1) * 1e3 / n_pcie
 
-    # A cold-cache check: before each of 5 K/V launches, a 1 GiB read (a sum)
-    # evicts the Infinity Cache and the L2s without leaving dirty lines behind.
+    # Cold caches: before each of 50 reps, a 1 GiB read (a sum) evicts the
+    # Infinity Cache and the L2s without leaving dirty lines behind; events
+    # then bracket compile + K/V (and the K/V launch alone).
     flush_buf = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
-    cold = []
-    for i in range(5):
-        flush_buf.sum()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        sets[i % S].kv()
-        b.record()
-        cold.append((a, b))
-    torch.cuda.synchronize()
-    kv_cold_ms = sorted(a.elapsed_time(b) for a, b in cold)[2]
+    median = lambda xs: sorted(xs)[len(xs) // 2]
+
+    def bracketed(n, flush, with_compile):
+        pairs = event_pairs(n * KV_EVENT_EVERY)
+        for i in range(n):
+            st = sets[i % S]
+            if flush:
+                flush_buf.sum()
+            elif not with_compile:
+                st.compile()
+            a, b = pairs[i]
+            a.record()
+            if with_compile:
+                st.compile()
+            st.kv()
+            b.record()
+            st.gather()
+        torch.cuda.synchronize()
+        return median([a.elapsed_time(b) for a, b in pairs])
+
+    kv_cold_ms = bracketed(20, True, False)
+    ck_cold_ms = bracketed(50, True, True)
+    ck_warm_ms = bracketed(50, False, True)
     del flush_buf
+    ceiling = copy_ceiling(ric, torch, sets, w0, sb)
 
     calib = calibrate_copy(ric, torch, runner.current_stream()) if args.calibrate_copy else None
 
@@ -425,7 +516,17 @@ def main():
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": load_traffic(kv_kernel_name(w0, sb["N"]), args.config),
                      "kernel": kv_kernel_name(w0, sb["N"]), "kv_flags": sets[0].kv_flags,
                      "bytes_per_launch": sb["kv"],
-                     "avg_launch_us": kv_mean * 1e3, "event_samples": len(ev)},
+                     "avg_launch_us": kv_mean * 1e3, "event_samples": len(ev),
+                     "frac_of_copy_ceiling": achieved / max(ceiling["torch_copy_gbps"],
+                                                            ceiling["identity_slots_gbps"])},
+        "copy_ceiling": ceiling,
+        "compile_plus_kv": {"bytes": sb["compile"] + sb["kv"],
+                            "warm_us": ck_warm_ms * 1e3,
+                            "warm_frac_of_peak": (sb["compile"] + sb["kv"]) / (ck_warm_ms * 1e-3) / 1e9
+                            / HBM_PEAK_GBPS,
+                            "after_cache_flush_us": ck_cold_ms * 1e3,
+                            "after_cache_flush_frac_of_peak": (sb["compile"] + sb["kv"]) / (ck_cold_ms * 1e-3)
+                            / 1e9 / HBM_PEAK_GBPS},
         "step_bytes": sb["total"],
         "step_gbps": sb["total"] / (ms_per_step * 1e-3) / 1e9,
         "step_frac_of_peak": sb["total"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
@@ -434,6 +535,9 @@ def main():
         "kernels_us": {"compile": mean(comp_ms) * 1e3, "kv_scatter": kv_mean * 1e3,
                        "gather": mean(ga_ms) * 1e3, "kv_scatter_after_cache_flush": kv_cold_ms * 1e3},
         "pcie_inclusive_tokens_per_s": N / (pcie_ms * 1e-3),
+        "condense": ({"us_with_host_planning_and_pair_upload": mean([st.condense["us"] for st in sets]),
+                      "rows_moved": sets[0].condense["rows_moved"], "bytes": sets[0].condense["bytes"],
+                      "instances": S} if sets[0].condense else None),
         "setup_s": setup_s,
     }
     if calib:
