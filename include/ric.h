@@ -263,7 +263,8 @@ int ric_spec_decode_metadata(ric_batch* b, const int32_t* num_draft_tokens, ric_
  * kernel of block size Bk, [P1 §混合 KV Cache]: [0,1,2] -> [0..5] for k = 2).
  * Entries past a row's own (expanded) blocks are set to `fill` (nano-vllm pads
  * with -1, [P5 prepare_block_tables]).  dst: DEVICE int32[R][width],
- * width <= k * the group's table capacity.  The persistent table itself
+ * width <= k * the group's table capacity, and k * the group's pool size must
+ * stay below 2^31 (expanded ids are int32).  The persistent table itself
  * (ric_get_columns, group 0) can be used directly when stale entries past
  * each row's count are acceptable.  Errors: ESTATE (no schedule since the
  * last row change), EINVAL. */

@@ -775,6 +775,8 @@ int ric_block_table_padded(ric_batch* b, int32_t group, int32_t ratio, int32_t w
     if (!b->scheduled) return fail(RIC_ESTATE, "ric_schedule must follow the last row change");
     if (group < 0 || group >= b->L.groups) return fail(RIC_EINVAL, "group %d outside [0, %d)", group, b->L.groups);
     if (ratio < 1) return fail(RIC_EINVAL, "kernel_blocks_per_block %d < 1", ratio);
+    if ((int64_t)group_pool(b->cfg, group) * ratio >= (int64_t(1) << 31))
+        return fail(RIC_EINVAL, "kernel_blocks_per_block %d: expanded block ids would not fit in int32", ratio);
     const int64_t cap = (int64_t)ratio * group_cap(b->cfg, group);
     if (width < 0 || width > cap) return fail(RIC_EINVAL, "width %d outside [0, %lld]", width, (long long)cap);
     if (width > 0 && b->sched_R > 0 && !dst) return fail(RIC_EINVAL, "dst is NULL");

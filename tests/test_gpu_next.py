@@ -51,6 +51,15 @@ def test_padded_block_table_needs_a_schedule(rt):
     with pytest.raises(ric.RicError) as e:
         ric.ric_block_table_padded(b.h, 4, -1, 0)
     assert e.value.code == ric.RIC_ESTATE
+    b.schedule_from(w)
+    dst = torch.zeros((3, 4), dtype=torch.int32, device="cuda")
+    for kw in (dict(group=1), dict(group=-1), dict(kernel_blocks_per_block=0),
+               dict(kernel_blocks_per_block=1 << 30)):          # expanded ids would overflow int32
+        with pytest.raises(ric.RicError) as e:
+            ric.ric_block_table_padded(b.h, 4, -1, dst.data_ptr(), **kw)
+        assert e.value.code == ric.RIC_EINVAL, kw
+    with pytest.raises(ric.RicError):
+        ric.ric_block_table_padded(b.h, w.max_blocks_per_req + 1, -1, dst.data_ptr())   # wider than the table
     b.close()
 
 
