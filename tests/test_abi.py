@@ -166,3 +166,21 @@ def test_workspace_fits(ric, name):
     nbytes = ric.ric_workspace_bytes(_cfg(ric, w))
     table = w.max_num_reqs * (w.max_model_len + w.max_blocks_per_req) * 4
     assert table <= nbytes < table + (64 << 20)
+
+
+def build_c_step(out_path, ric):
+    """Compile the plain-C step program against the library and ric.h."""
+    src = os.path.join(ROOT, "tests", "c_abi_step.c")
+    libdir = os.path.dirname(ric.LIB_PATH)
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                    "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", src, "-o", str(out_path),
+                    "-L", libdir, "-lric", "-L", "/opt/rocm/lib", "-lamdhip64", f"-Wl,-rpath,{libdir}"],
+                   check=True, capture_output=True, text=True)
+    return str(out_path)
+
+
+def test_header_is_plain_c_and_links_from_c(ric, tmp_path):
+    """ric.h compiles as C99 and a C program links against libric.so with
+    no C++ runtime of its own (the GPU test runs it)."""
+    exe = build_c_step(tmp_path / "c_abi_step", ric)
+    assert os.path.getsize(exe) > 0

@@ -12,6 +12,7 @@ import torch
 import workloads
 from oracle import batch as ref_batch, cbind, step as ref_step, vectorised
 from tests.gpu_helpers import assert_step_equal, expected_step, read_rows_i32, replay_history
+from tests.oracle_helpers import golden
 
 pytestmark = pytest.mark.gpu
 
@@ -563,3 +564,31 @@ def test_strided_sources_from_a_fused_qkv_tensor(rt):
     assert torch.equal(flat_k[slots], k[:N].reshape(N, -1).view(torch.int16))
     assert torch.equal(flat_v[slots], v[:N].reshape(N, -1).view(torch.int16))
     b.close()
+
+
+def test_c_program_through_the_abi(rt, tmp_path):
+    """A plain-C program (tests/c_abi_step.c) runs the first page's worked
+    example through ric.h: its printed outputs equal the page's values, and
+    its K/V rows land at the printed slots."""
+    import json
+    import subprocess
+    from tests.test_abi import build_c_step
+    ric, runner = rt
+    exe = build_c_step(tmp_path / "c_abi_step", ric)
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert run.returncode == 0, run.stderr[-2000:]
+    got = json.loads(run.stdout)
+    g = golden("p1_worked_example.json")["expect"]
+    N = 6
+    assert (got["num_reqs"], got["num_actual_tokens"], got["num_tokens_padded"]) == (3, N, 8)
+    for k in ("query_start_loc", "seq_lens", "logits_indices"):
+        assert got[k] == g[k], k
+    for k in ("req_indices", "positions", "input_ids", "slot_mapping"):
+        assert got[k][:N] == g[k], k
+    assert got["req_indices"][N:] == [-1, -1] and got["slot_mapping"][N:] == [0, 0]
+    assert got["cu_seqlens_k"] == [0, 6, 9, 19]
+    assert got["sample_indices"] == [0, 5, -1]          # B's chunk is discarded
+    first = got["k_cache_first_byte"]
+    for t, s in enumerate(g["slot_mapping"]):
+        assert first[s] == t + 1
+    assert all(first[i] == 0 for i in range(4, len(first)) if i not in g["slot_mapping"])
