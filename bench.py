@@ -114,6 +114,54 @@ def load_traffic(kernel_name, workload_name):
     return int(traffic.group(1))
 
 
+class Event:
+    """A HIP timing event created with hipEventDisableSystemFence.  Recording a
+    default event (torch.cuda.Event) performs a system-scope release: the L2s
+    are written back and invalidated, which lengthens the bracketed interval by
+    1-2 us and slows the next kernel.  These events only timestamp.  They are
+    recorded on `Event.stream` (the library's stream) through the HIP runtime
+    that torch already loaded (the same library instance libric uses)."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+    stream = None
+    _hip = None
+
+    @classmethod
+    def _lib(cls):
+        if cls._hip is None:
+            paths = [line.split()[-1] for line in open("/proc/self/maps") if "libamdhip64" in line]
+            if not paths:
+                raise RuntimeError("the HIP runtime is not loaded in this process")
+            lib = ctypes.CDLL(paths[0])
+            vp = ctypes.c_void_p
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
+            lib.hipEventRecord.argtypes = [vp, vp]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+            lib.hipEventDestroy.argtypes = [vp]
+            cls._hip = lib
+        return cls._hip
+
+    def __init__(self):
+        self.h = ctypes.c_void_p()
+        if self._lib().hipEventCreateWithFlags(ctypes.byref(self.h), self.DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        self._rec = self._hip.hipEventRecord
+        self._st = ctypes.c_void_p(Event.stream or None)
+
+    def record(self):
+        if self._rec(self.h, self._st) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_time(self, end):
+        ms = ctypes.c_float()
+        if self._hip.hipEventElapsedTime(ctypes.byref(ms), self.h, end.h) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        if self.h and self._hip is not None:
+            self._hip.hipEventDestroy(self.h)
+
+
 class GpuStep:
     """Prebuilt library calls for one rotation instance."""
 
@@ -174,7 +222,7 @@ class GpuStep:
         nbytes = sum(2 * (4 * len(by_id[by_row[src]].tokens) + 4 * len(by_id[by_row[src]].blocks) + 4 * 12)
                      for _, src in plan)
         torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a, b = Event(), Event()
         a.record()
         moved = ric.ric_condense(h)
         b.record()
@@ -195,9 +243,9 @@ class GpuStep:
 
     def reschedule(self):
         """Host counts -> pinned staging (uploaded by the next compile)."""
-        live_rows = self.batch.row_order()
-        by_id = self.w.by_id()
-        if not hasattr(self, "_sched"):
+        if not hasattr(self, "_sched"):          # the counts a scheduler would hand over, built once
+            live_rows = self.batch.row_order()
+            by_id = self.w.by_id()
             c = [by_id[i].num_computed for i in live_rows]
             q = [by_id[i].num_scheduled for i in live_rows]
             self._sched = [self.ric._i32(c), self.ric._i32(q)]
@@ -301,7 +349,7 @@ def copy_ceiling(ric, torch, sets, w, sb, reps=20):
     times = []
     for i in range(reps + 2):
         src, dst = bufs[i % pairs]
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a, b = Event(), Event()
         a.record()
         dst.copy_(src)
         b.record()
@@ -322,7 +370,7 @@ def copy_ceiling(ric, torch, sets, w, sb, reps=20):
         args = list(sets[k].kv_args)
         args[5] = ctypes.c_void_p(slots[k].data_ptr())
         args[11] = ric.RIC_KV_LONG_RUNS
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a, b = Event(), Event()
         a.record()
         sets[k]._check(sets[k].lib.ric_reshape_and_cache(*args))
         b.record()
@@ -342,7 +390,7 @@ def calibrate_copy(ric, torch, stream):
     idx = torch.arange(rows, dtype=torch.int32, device="cuda")
     times = []
     for _ in range(5):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a, b = Event(), Event()
         a.record()
         ric.ric_gather_rows(src.data_ptr(), row, rows, idx.data_ptr(), 0, rows, row, dst.data_ptr(), row, 0, stream)
         b.record()
@@ -371,6 +419,7 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    Event.stream = runner.current_stream()     # every library call below runs on this stream
     w0 = workloads.get(args.config)
     sb = step_bytes(w0)
     S = args.sets or max(2, min(16, math.ceil((1 << 30) / sb["total"])))
@@ -390,7 +439,7 @@ def main():
     setup_s = time.perf_counter() - t_setup
 
     def event_pairs(n):
-        return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        return [(Event(), Event())
                 for _ in range((n + KV_EVENT_EVERY - 1) // KV_EVENT_EVERY)]
 
     def run(n, mode, pool=None):
@@ -418,7 +467,7 @@ def main():
                 st.gather()
                 ev.append((a, b))
             else:
-                e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+                e = [Event() for _ in range(6)]
                 e[0].record(); st.compile(); e[1].record()
                 e[2].record(); st.kv(); e[3].record()
                 e[4].record(); st.gather(); e[5].record()
@@ -451,6 +500,9 @@ def main():
 
     # Same step with the counts uploaded from the host first (schedule + the
     # flush inside compile carry them over PCIe).
+    for st in sets:                      # builds each instance's host count arrays once
+        st.reschedule()
+        st.compile()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     n_pcie = max(args.steps // 2, 1)

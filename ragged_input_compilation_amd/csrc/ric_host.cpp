@@ -465,7 +465,11 @@ int ric_create(const ric_config* cfg, void* stream, void* workspace, size_t work
         if (hipHostMalloc(&p, L.staging_bytes, hipHostMallocDefault) != hipSuccess)
             return bail(fail(RIC_ENOMEM, "pinned staging allocation failed"));
         b->h_log[i] = static_cast<uint8_t*>(p);
-        if (hipEventCreateWithFlags(&b->ev[i], hipEventDisableTiming) != hipSuccess)
+        // These events only tell the host when a log's upload has finished
+        // reading it; no device write needs to become visible to the host, so
+        // they skip the system-scope fence (an L2 write-back and invalidate
+        // on every flush otherwise).
+        if (hipEventCreateWithFlags(&b->ev[i], hipEventDisableTiming | hipEventDisableSystemFence) != hipSuccess)
             return bail(fail(RIC_EHIP, "event creation failed"));
     }
     const int MR = cfg->max_num_reqs;
