@@ -321,10 +321,12 @@ int ric_compile(ric_batch* b, int32_t num_tokens_padded, ric_step* out);
  *                     slot is outside [0, num_slots) (that row is not written)
  *   flags             0, or RIC_KV_LONG_RUNS: a performance hint that most
  *                     consecutive tokens go to consecutive slots (prefill
- *                     chunks; e.g. num_actual_tokens / num_reqs >= 64).  It
- *                     selects streaming loads, measured ~4% faster on long
- *                     runs and ~20% slower on scattered decode slots; results
- *                     are identical either way.
+ *                     chunks; e.g. num_actual_tokens / num_reqs >= 64) in a
+ *                     launch that moves at least ~256 MB.  It selects
+ *                     streaming loads for launches above 2048 tokens:
+ *                     measured 1-5% faster there, but 8-10% slower on
+ *                     smaller launches and ~20% slower on scattered decode
+ *                     slots.  Results are identical either way.
  * All layers are written by one launch.  Errors: EINVAL (alignment, counts,
  * unknown flags), EHIP. */
 #define RIC_KV_LONG_RUNS 1u
