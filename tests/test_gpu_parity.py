@@ -234,6 +234,37 @@ def test_bruteforce_tiny_batches(rt):
         b.close()
 
 
+def test_random_medium_batches(rt):
+    """Forty seeded batches between the tiny cases and the named workloads:
+    up to 400 requests, decode-only to 600-token chunks, cached prefixes up to
+    3000, block sizes from 1 to 128 (powers of two and not), padded sizes up to
+    256 above N, and table payloads that overflow the default staging log.
+    Every compile output equals the C oracle's; every fifth batch also checks
+    every cache byte outside the null block."""
+    ric, runner = rt
+    rng = np.random.default_rng(1234)
+    for trial in range(40):
+        B = int(rng.choice([1, 3, 5, 7, 16, 32, 64, 100, 128]))
+        R = int(rng.integers(1, 401))
+        max_q = int(rng.choice([1, 8, 64, 600]))
+        M = 4096
+        pool = R * -(-(3000 + max_q) // B) + 10
+        reqs = workloads.random_batch(rng, num_reqs=R, block_size=B, max_model_len=M, num_kv_blocks=pool,
+                                      max_q=max_q, max_c=3000)
+        N = sum(r.num_scheduled for r in reqs)
+        n_pad = N + int(rng.integers(0, 257))
+        w = workloads.Workload("medium", block_size=B, max_num_reqs=R + int(rng.integers(0, 50)), max_model_len=M,
+                               max_blocks_per_req=-(-M // B), max_num_batched_tokens=n_pad, num_kv_blocks=pool,
+                               kv_heads=1, head_dim=8, kv_dtype="f16", num_layers=1, hidden_size=64, gather="all",
+                               initial=reqs, capture_sizes=[n_pad], seed=int(rng.integers(1 << 30)))
+        label = f"trial {trial}: B={B} R={R} max_q={max_q} N={N} n_pad={n_pad}"
+        b, s, ref, order, exp, _ = _compile(rt, w)
+        assert_step_equal(b.step_outputs(s), exp, label)
+        if trial % 5 == 0:
+            _full_kv_check(rt, w, b, s, exp)
+        b.close()
+
+
 def test_empty_batch_is_all_padding(rt):
     ric, runner = rt
     cfg = ric.make_config(max_num_reqs=4, max_model_len=16, block_size=4, max_blocks_per_req=4,
