@@ -235,7 +235,7 @@ def test_bruteforce_tiny_batches(rt):
 
 
 def test_random_medium_batches(rt):
-    """Forty seeded batches between the tiny cases and the named workloads:
+    """A hundred seeded batches between the tiny cases and the named workloads:
     up to 400 requests, decode-only to 600-token chunks, cached prefixes up to
     3000, block sizes from 1 to 128 (powers of two and not), padded sizes up to
     256 above N, and table payloads that overflow the default staging log.
@@ -243,7 +243,7 @@ def test_random_medium_batches(rt):
     every cache byte outside the null block."""
     ric, runner = rt
     rng = np.random.default_rng(1234)
-    for trial in range(40):
+    for trial in range(100):
         B = int(rng.choice([1, 3, 5, 7, 16, 32, 64, 100, 128]))
         R = int(rng.integers(1, 401))
         max_q = int(rng.choice([1, 8, 64, 600]))
