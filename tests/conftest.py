@@ -12,14 +12,9 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
 
 
-def pytest_collection_modifyitems(config, items):
-    # GPU tests run in file order; nothing to reorder.  Report the test name
-    # before each GPU test so a fault on the box names its case.
-    pass
-
-
 @pytest.fixture(autouse=True)
 def _announce(request):
+    # Name each GPU test before it runs, so that a device fault names its case.
     if request.node.get_closest_marker("gpu") is not None:
         print(f"\n[gpu-test] {request.node.nodeid}", flush=True)
     yield
