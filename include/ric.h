@@ -26,6 +26,11 @@
  *     the step path (schedule, compile, reshape_and_cache, gather) waits for
  *     the device or copies device data to the host.
  *   - Integer values are int32; byte offsets are computed in 64 bits.
+ *   - A handle belongs to the device that was current at ric_create; calls on
+ *     it make that device current for their duration and restore the
+ *     caller's.  Calls without a handle (ric_reshape_and_cache,
+ *     ric_gather_rows) run on the current device, whose stream they take.
+ *   - A handle is not thread-safe: one thread at a time per handle.
  */
 #ifndef RIC_H
 #define RIC_H

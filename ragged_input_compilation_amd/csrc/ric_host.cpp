@@ -244,6 +244,22 @@ struct ric_batch {
 
 namespace {
 
+// Makes the handle's device current for one call (and restores the caller's),
+// so a process that drives handles on several GPUs needs no device switching
+// of its own around library calls.
+struct DeviceScope {
+    int prev = -1;
+    explicit DeviceScope(const ric_batch* b) {
+        int cur = -1;
+        if (hipGetDevice(&cur) == hipSuccess && cur != b->device && hipSetDevice(b->device) == hipSuccess) prev = cur;
+    }
+    ~DeviceScope() {
+        if (prev >= 0) (void)hipSetDevice(prev);
+    }
+    DeviceScope(const DeviceScope&) = delete;
+    DeviceScope& operator=(const DeviceScope&) = delete;
+};
+
 // Bytes the log needs for everything staged so far plus `extra_words` more
 // payload in one more op, plus the scalar columns a flush appends.
 size_t log_need(const ric_batch* b, size_t extra_words, size_t extra_ops) {
@@ -495,6 +511,7 @@ int ric_create(const ric_config* cfg, void* stream, void* workspace, size_t work
 
 int ric_destroy(ric_batch* b) {
     if (!b) return RIC_OK;
+    DeviceScope ds(b);
     if (b->ws) (void)hipStreamSynchronize(b->stream);
     for (int i = 0; i < 2; ++i) {
         if (b->ev[i]) (void)hipEventDestroy(b->ev[i]);
@@ -507,6 +524,7 @@ int ric_destroy(ric_batch* b) {
 
 int ric_set_stream(ric_batch* b, void* stream) {
     if (!b) return fail(RIC_EINVAL, "handle is NULL");
+    DeviceScope ds(b);
     HIP_TRY(hipStreamSynchronize(b->stream));
     b->stream = static_cast<hipStream_t>(stream);
     return RIC_OK;
@@ -516,6 +534,7 @@ int ric_add_request(ric_batch* b, uint64_t req_id, const int32_t* tokens, int32_
                     int32_t num_prompt, int32_t num_computed, const int32_t* blocks, int32_t num_blocks,
                     const ric_sampling* sampling, int32_t* out_row) {
     if (!b) return fail(RIC_EINVAL, "handle is NULL");
+    DeviceScope ds(b);
     if (b->row_of.count(req_id)) return fail(RIC_EEXIST, "request id %llu is live", (unsigned long long)req_id);
     if (num_tokens < 0 || num_tokens > b->cfg.max_model_len)
         return fail(RIC_ERANGE, "num_tokens %d outside [0, max_model_len %d]", num_tokens, b->cfg.max_model_len);
@@ -573,6 +592,7 @@ int ric_remove_request(ric_batch* b, uint64_t req_id, int32_t* out_row) {
 
 int ric_append_tokens(ric_batch* b, uint64_t req_id, const int32_t* ids, int32_t n) {
     if (!b) return fail(RIC_EINVAL, "handle is NULL");
+    DeviceScope ds(b);
     int32_t row;
     int rc = find(b, req_id, &row);
     if (rc) return rc;
@@ -591,6 +611,7 @@ int ric_append_tokens(ric_batch* b, uint64_t req_id, const int32_t* ids, int32_t
 
 static int set_blocks(ric_batch* b, uint64_t req_id, int32_t g, const int32_t* ids, int32_t n, bool replace) {
     if (!b) return fail(RIC_EINVAL, "handle is NULL");
+    DeviceScope ds(b);
     if (g < 0 || g >= b->L.groups) return fail(RIC_EINVAL, "group %d outside [0, %d)", g, b->L.groups);
     int32_t row;
     int rc = find(b, req_id, &row);
@@ -650,6 +671,7 @@ int32_t ric_condense_plan(const uint8_t* live, int32_t num_rows, int32_t* holes,
 
 int ric_condense(ric_batch* b, int32_t* out_num_moved) {
     if (!b) return fail(RIC_EINVAL, "handle is NULL");
+    DeviceScope ds(b);
     const int MR = b->cfg.max_num_reqs;
     std::vector<int32_t> holes(MR), srcs(MR);
     const int32_t np = ric_condense_plan(b->live.data(), MR, holes.data(), srcs.data());
@@ -699,6 +721,7 @@ int ric_condense(ric_batch* b, int32_t* out_num_moved) {
 int ric_append_sampled(ric_batch* b, int32_t n, const int32_t* rows, const int32_t* src_index,
                        const int32_t* dev_tokens, int32_t dev_tokens_len) {
     if (!b) return fail(RIC_EINVAL, "handle is NULL");
+    DeviceScope ds(b);
     if (n < 0 || n > b->cfg.max_num_reqs) return fail(RIC_EINVAL, "n %d outside [0, max_num_reqs]", n);
     if (n == 0) return RIC_OK;
     if (!rows || !dev_tokens || dev_tokens_len <= 0) return fail(RIC_EINVAL, "NULL or empty argument");
@@ -735,6 +758,7 @@ int ric_append_sampled(ric_batch* b, int32_t n, const int32_t* rows, const int32
 
 int ric_spec_decode_metadata(ric_batch* b, const int32_t* num_draft_tokens, ric_spec_decode* out) {
     if (!b || !out) return fail(RIC_EINVAL, "NULL argument");
+    DeviceScope ds(b);
     if (!b->scheduled || !b->compiled) return fail(RIC_ESTATE, "needs a compile of the current schedule");
     const int32_t R = b->sched_R;
     if (R > 0 && !num_draft_tokens) return fail(RIC_EINVAL, "num_draft_tokens is NULL");
@@ -776,6 +800,7 @@ int ric_spec_decode_metadata(ric_batch* b, const int32_t* num_draft_tokens, ric_
 
 int ric_block_table_padded(ric_batch* b, int32_t group, int32_t ratio, int32_t width, int32_t fill, int32_t* dst) {
     if (!b) return fail(RIC_EINVAL, "handle is NULL");
+    DeviceScope ds(b);
     if (!b->scheduled) return fail(RIC_ESTATE, "ric_schedule must follow the last row change");
     if (group < 0 || group >= b->L.groups) return fail(RIC_EINVAL, "group %d outside [0, %d)", group, b->L.groups);
     if (ratio < 1) return fail(RIC_EINVAL, "kernel_blocks_per_block %d < 1", ratio);
@@ -801,6 +826,7 @@ int ric_block_table_padded(ric_batch* b, int32_t group, int32_t ratio, int32_t w
 
 int ric_flush(ric_batch* b) {
     if (!b) return fail(RIC_EINVAL, "handle is NULL");
+    DeviceScope ds(b);
     return flush(b);
 }
 
@@ -841,6 +867,7 @@ int ric_get_columns(const ric_batch* b, ric_columns* o) {
 
 int ric_sync(ric_batch* b) {
     if (!b) return fail(RIC_EINVAL, "handle is NULL");
+    DeviceScope ds(b);
     HIP_TRY(hipStreamSynchronize(b->stream));
     return RIC_OK;
 }
@@ -878,6 +905,7 @@ int ric_check_step(const ric_config* cfg, int32_t R, const int32_t* c, const int
 
 int ric_schedule(ric_batch* b, int32_t R, const int32_t* c, const int32_t* q) {
     if (!b) return fail(RIC_EINVAL, "handle is NULL");
+    DeviceScope ds(b);
     if (R != b->num_live) return fail(RIC_EINVAL, "num_reqs %d but %d requests are live", R, b->num_live);
     if (b->used_rows() != R) return fail(RIC_ESTATE, "rows are not condensed: live rows must be [0, %d)", R);
     const int MR = b->cfg.max_num_reqs;
@@ -916,6 +944,7 @@ int ric_schedule(ric_batch* b, int32_t R, const int32_t* c, const int32_t* q) {
 
 int ric_compile(ric_batch* b, int32_t n_pad, ric_step* out) {
     if (!b) return fail(RIC_EINVAL, "handle is NULL");
+    DeviceScope ds(b);
     if (!b->scheduled) return fail(RIC_ESTATE, "ric_schedule must follow the last row change");
     if (n_pad < b->sched_N || n_pad > b->cfg.max_num_batched_tokens)
         return fail(RIC_EINVAL, "num_tokens_padded %d outside [N=%d, max_num_batched_tokens=%d]", n_pad,
