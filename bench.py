@@ -198,7 +198,11 @@ class GpuStep:
         if w.gather == "all":
             idx, cnt, rows = self.step.logits_indices, None, len(live)
         else:
-            idx, cnt, rows = self.step.sample_indices, self.step.dev_scalars + 20, w.max_num_reqs
+            # the compacted rows; the host already knows how many there are (the
+            # schedule's num_sampled), so a step where no request completes its
+            # prompt launches no gather (the device count serves callers that
+            # do not know it)
+            idx, cnt, rows = self.step.sample_indices, None, self.step.num_sampled
         self.gather_args = [ctypes.c_void_p(hidden.data_ptr()), row, hidden.shape[0], ctypes.c_void_p(idx),
                             ctypes.c_void_p(cnt), rows, row, ctypes.c_void_p(out.data_ptr()), row, None, st]
         self.h = ctypes.c_void_p(self.batch.h)
