@@ -17,7 +17,9 @@
  * Conventions for every call:
  *   - Return value: RIC_OK (0) or a negative RIC_E* code.  On error nothing
  *     has changed (no host state, no device work enqueued) and
- *     ric_last_error() holds a message for the calling thread.
+ *     ric_last_error() holds a message for the calling thread; the one
+ *     exception is RIC_EHIP, a failure reported by the HIP runtime, which may
+ *     come after part of a call's device work was enqueued.
  *   - "device" pointers are HIP device addresses (e.g. torch tensor
  *     data_ptr()); "host" pointers are ordinary host memory.  Host input arrays
  *     are read (and copied into pinned staging where needed) before the call
@@ -332,8 +334,9 @@ int ric_compile(ric_batch* b, int32_t num_tokens_padded, ric_step* out);
  *                     measured 1-5% faster there, but 8-10% slower on
  *                     smaller launches and ~20% slower on scattered decode
  *                     slots.  Results are identical either way.
- * All layers are written by one launch.  Errors: EINVAL (alignment, counts,
- * unknown flags), EHIP. */
+ * Up to 32 layers are written by one launch (more layers: one launch per 32).
+ * num_tokens <= 2^24 per call.
+ * Errors: EINVAL (alignment, counts, unknown flags), EHIP. */
 #define RIC_KV_LONG_RUNS 1u
 int ric_reshape_and_cache(const void* const* k, const void* const* v, void* const* k_cache,
                           void* const* v_cache, int32_t num_layers, const int32_t* slot_mapping,
@@ -346,7 +349,8 @@ int ric_reshape_and_cache(const void* const* k, const void* const* v, void* cons
  * index >= src_rows yields a zero row and bumps *dev_status if given.  Rows
  * m in [count, max_rows) of dst are left untouched.  Used for hidden states at
  * logits_indices / sample_indices ([P2 §8.7], [P4 §4.1]).  Pointers and
- * strides 16-byte aligned, row_bytes a multiple of 16.  Errors: EINVAL, EHIP. */
+ * strides 16-byte aligned, row_bytes a multiple of 16, max_rows <= 2^24.
+ * Errors: EINVAL, EHIP. */
 int ric_gather_rows(const void* src, int64_t src_row_stride, int64_t src_rows,
                     const int32_t* idx, const int32_t* dev_count, int32_t max_rows,
                     int32_t row_bytes, void* dst, int64_t dst_row_stride, int32_t* dev_status,

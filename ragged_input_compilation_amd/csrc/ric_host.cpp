@@ -51,6 +51,7 @@ int fail(int code, const char* fmt, ...) {
     } while (0)
 
 constexpr size_t kAlign = 256;
+constexpr int32_t kMaxRowsPerLaunch = 1 << 24;   // rows * 256 lanes must fit a 32-bit work-item count
 constexpr uint32_t kMaxWordsPerOp = 8192;   // split big payloads so ops spread over workgroups
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -1022,6 +1023,9 @@ int ric_reshape_and_cache(const void* const* k, const void* const* v, void* cons
     if (num_layers < 0 || num_tokens < 0) return fail(RIC_EINVAL, "negative count");
     if (flags & ~RIC_KV_LONG_RUNS) return fail(RIC_EINVAL, "unknown flags 0x%x", flags);
     if (num_layers == 0 || num_tokens == 0) return RIC_OK;
+    if (num_tokens > kMaxRowsPerLaunch)
+        return fail(RIC_EINVAL, "num_tokens %d above %d per call (the grid counts work-items in 32 bits)",
+                    num_tokens, kMaxRowsPerLaunch);
     if (!k || !v || !k_cache || !v_cache || !slot_mapping) return fail(RIC_EINVAL, "NULL pointer argument");
     if (row_bytes <= 0 || row_bytes % 16 != 0) return fail(RIC_EINVAL, "row_bytes %d not a positive multiple of 16", row_bytes);
     if (src_row_stride == 0) src_row_stride = row_bytes;
@@ -1061,6 +1065,9 @@ int ric_gather_rows(const void* src, int64_t src_row_stride, int64_t src_rows, c
                     int64_t dst_row_stride, int32_t* dev_status, void* stream) {
     if (max_rows < 0) return fail(RIC_EINVAL, "max_rows negative");
     if (max_rows == 0) return RIC_OK;
+    if (max_rows > kMaxRowsPerLaunch)
+        return fail(RIC_EINVAL, "max_rows %d above %d per call (the grid counts work-items in 32 bits)", max_rows,
+                    kMaxRowsPerLaunch);
     if (!src || !idx || !dst) return fail(RIC_EINVAL, "NULL pointer argument");
     if (row_bytes <= 0 || row_bytes % 16 != 0) return fail(RIC_EINVAL, "row_bytes %d not a positive multiple of 16", row_bytes);
     if (src_row_stride == 0) src_row_stride = row_bytes;
