@@ -392,6 +392,80 @@ def copy_ceiling(ric, torch, sets, w, sb, reps=20):
                 identity_slots_us=t_ident * 1e3, identity_slots_gbps=sb["kv"] / (t_ident * 1e-3) / 1e9)
 
 
+def next_rows(ric, runner, torch, w, st, reps=20):
+    """Times of the calls beyond the step (untimed diagnostics, events around
+    each call; a call that stages host data includes that host work): the
+    dense padded block table, the speculative-decoding indices, the device-side
+    append of sampled tokens, and the compile with a second KV-cache group that
+    gets its own slots.  cu_seqlens_k is part of every compile."""
+    median = lambda xs: sorted(xs)[len(xs) // 2]
+
+    def timed(fn):
+        pairs = []
+        for _ in range(reps):
+            a, b = Event(), Event()
+            a.record()
+            fn()
+            b.record()
+            pairs.append((a, b))
+        torch.cuda.synchronize()
+        return median([a.elapsed_time(b) for a, b in pairs]) * 1e3
+
+    out = {}
+    h = st.batch.h
+    live = w.live_requests()
+    by_id = w.by_id()
+    order = st.batch.row_order()
+    R = len(order)
+    nb = [len(by_id[i].blocks) for i in order]
+    width = max(nb)
+    dst = torch.empty((R, width), dtype=torch.int32, device="cuda")
+    us = timed(lambda: ric.ric_block_table_padded(h, width, -1, dst.data_ptr()))
+    nbytes = 4 * R + 4 * sum(nb) + 4 * R * width
+    out["padded_block_table"] = dict(rows=R, width=width, us=us, bytes=nbytes, gbps=nbytes / (us * 1e-6) / 1e9)
+
+    q = [by_id[i].num_scheduled for i in order]
+    d = [min(x - 1, 3) for x in q]
+    m = ric.ric_spec_decode_metadata(h, d)
+    us = timed(lambda: ric.ric_spec_decode_metadata(h, d))
+    nbytes = 4 * R + 4 * (R + 1) + 4 * m.num_draft_tokens + 4 * m.num_logits + 4 * (R + 1) + \
+        8 * m.num_draft_tokens + 4 * R
+    out["spec_decode"] = dict(num_logits=m.num_logits, num_draft=m.num_draft_tokens, us_per_call=us, bytes=nbytes)
+
+    b2 = runner.Batch(runner.config_of(w))
+    b2.load_history(w)
+    rows = [r for r, rid in enumerate(b2.row_order()) if len(by_id[rid].tokens) + reps + 2 <= w.max_model_len]
+    if rows:
+        sampled = torch.randint(0, 1 << 20, (len(rows),), dtype=torch.int32, device="cuda")
+        src = list(reversed(range(len(rows))))
+        us = timed(lambda: ric.ric_append_sampled(b2.h, rows, sampled.data_ptr(), len(rows), src))
+        out["append_sampled"] = dict(rows=len(rows), us_per_call=us, bytes=20 * len(rows))
+    else:
+        out["append_sampled"] = dict(rows=0, skipped="no row has room left in its token history")
+    b2.close()
+
+    # the compile with a second slotted group (the same block size and ids as
+    # group 0), against a batch built the same way with one group
+    us_by_groups = {}
+    for groups in (1, 2):
+        cfg = runner.config_of(w)
+        cfg.num_kv_groups = groups
+        cfg.group_block_size[1] = w.block_size
+        b3 = runner.Batch(cfg)
+        b3.load_history(w)
+        if groups == 2:
+            for rid in b3.row_order():
+                ric.ric_append_blocks_group(b3.h, rid, 1, by_id[rid].blocks)
+        b3.schedule_from(w)
+        ric.ric_compile(b3.h, st.n_pad)
+        us_by_groups[groups] = timed(lambda: ric.ric_compile(b3.h, st.n_pad))
+        b3.close()
+    N = sum(q)
+    out["compile_two_kv_groups"] = dict(us=us_by_groups[2], us_one_group=us_by_groups[1], extra_bytes=4 * N + 4 * sum(
+        -(-(r.num_computed + r.num_scheduled) // w.block_size) - r.num_computed // w.block_size for r in live))
+    return out
+
+
 def calibrate_copy(ric, torch, stream):
     """A plain copy of known size through the row-gather kernel with identity
     indices: 16384 rows of 16 KiB (256 MiB read, 256 MiB written)."""
@@ -555,6 +629,7 @@ def main():
     ck_warm_ms = bracketed(50, False, True)
     del flush_buf
     ceiling = copy_ceiling(ric, torch, sets, w0, sb)
+    nxt = next_rows(ric, runner, torch, w0, sets[0])
 
     calib = calibrate_copy(ric, torch, runner.current_stream()) if args.calibrate_copy else None
 
@@ -598,6 +673,7 @@ def main():
         "kernels_us": {"compile": mean(comp_ms) * 1e3, "kv_scatter": kv_mean * 1e3,
                        "gather": mean(ga_ms) * 1e3, "kv_scatter_after_cache_flush": kv_cold_ms * 1e3},
         "pcie_inclusive_tokens_per_s": N / (pcie_ms * 1e-3),
+        "next_rows": nxt,
         "condense": ({"us_with_host_planning_and_pair_upload": mean([st.condense["us"] for st in sets]),
                       "rows_moved": sets[0].condense["rows_moved"], "bytes": sets[0].condense["bytes"],
                       "instances": S} if sets[0].condense else None),
