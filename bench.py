@@ -203,6 +203,7 @@ class GpuStep:
             # prompt launches no gather (the device count serves callers that
             # do not know it)
             idx, cnt, rows = self.step.sample_indices, None, self.step.num_sampled
+        self.gather_rows = rows
         self.gather_args = [ctypes.c_void_p(hidden.data_ptr()), row, hidden.shape[0], ctypes.c_void_p(idx),
                             ctypes.c_void_p(cnt), rows, row, ctypes.c_void_p(out.data_ptr()), row, None, st]
         self.h = ctypes.c_void_p(self.batch.h)
@@ -671,7 +672,8 @@ def main():
         "ms_per_step_without_events": ms_no_events,
         "host_enqueue_us_per_step": host_ms * 1e3,
         "kernels_us": {"compile": mean(comp_ms) * 1e3, "kv_scatter": kv_mean * 1e3,
-                       "gather": mean(ga_ms) * 1e3, "kv_scatter_after_cache_flush": kv_cold_ms * 1e3},
+                       "gather": mean(ga_ms) * 1e3 if sets[0].gather_rows else None,
+                       "kv_scatter_after_cache_flush": kv_cold_ms * 1e3},
         "pcie_inclusive_tokens_per_s": N / (pcie_ms * 1e-3),
         "next_rows": nxt,
         "condense": ({"us_with_host_planning_and_pair_upload": mean([st.condense["us"] for st in sets]),
