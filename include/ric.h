@@ -147,6 +147,12 @@ typedef struct {
     float* temperature;
     float* top_p;
     float* repetition_penalty;
+    /* KV-cache groups: [g] block table, its row stride and its per-row valid
+     * count; [0] repeats blocks / block_stride / num_blocks; NULL and 0 for
+     * g >= num_kv_groups. */
+    int32_t* group_blocks[4];
+    int64_t group_block_stride[4];
+    int32_t* group_num_blocks[4];
 } ric_columns;
 
 /* ---- handle -------------------------------------------------------------- */

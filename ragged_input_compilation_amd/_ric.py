@@ -60,7 +60,9 @@ class ric_columns(ctypes.Structure):
     _fields_ = [("tokens", _vp), ("blocks", _vp), ("token_stride", ctypes.c_int64),
                 ("block_stride", ctypes.c_int64)] + \
                [(n, _vp) for n in ("num_tokens", "num_prompt", "num_computed", "num_scheduled",
-                                   "num_blocks", "top_k", "temperature", "top_p", "repetition_penalty")]
+                                   "num_blocks", "top_k", "temperature", "top_p", "repetition_penalty")] + \
+               [("group_blocks", _vp * 4), ("group_block_stride", ctypes.c_int64 * 4),
+                ("group_num_blocks", _vp * 4)]
 
 
 class ric_spec_decode(ctypes.Structure):

@@ -863,6 +863,12 @@ int ric_get_columns(const ric_batch* b, ric_columns* o) {
     o->temperature = reinterpret_cast<float*>(m->dcol(kTemperature));
     o->top_p = reinterpret_cast<float*>(m->dcol(kTopP));
     o->repetition_penalty = reinterpret_cast<float*>(m->dcol(kRepPenalty));
+    for (int g = 0; g < RIC_MAX_KV_GROUPS; ++g) {
+        const bool on = g < b->L.groups;
+        o->group_blocks[g] = on ? m->blk(g) : nullptr;
+        o->group_block_stride[g] = on ? m->bstride(g) : 0;
+        o->group_num_blocks[g] = on ? m->dcol(blocks_col(g)) : nullptr;
+    }
     return RIC_OK;
 }
 

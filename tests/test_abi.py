@@ -1,6 +1,7 @@
 """The C-ABI library on the CPU: it loads, exports every entry point the
 header declares, and its host-only helpers (padded size, condense plan, step
 check) agree with the oracle.  No device work is issued here."""
+import ctypes
 import os
 import re
 import subprocess
@@ -217,3 +218,30 @@ def test_binding_fails_loudly_without_the_library(tmp_path):
                        timeout=120, env={**os.environ, "PYTHONPATH": str(tmp_path)})
     assert r.returncode != 0
     assert "is not built" in r.stderr
+
+
+def test_struct_layouts_match_the_header(ric, tmp_path):
+    """Every field of the header's structs sits at the same offset, with the
+    same size, in the C compiler's layout and in the ctypes mirrors."""
+    structs = {"ric_config": ric.ric_config, "ric_sampling": ric.ric_sampling, "ric_step": ric.ric_step,
+               "ric_columns": ric.ric_columns, "ric_spec_decode": ric.ric_spec_decode}
+    lines = ["#include <stddef.h>", "#include <stdio.h>", '#include "ric.h"', "int main(void) {"]
+    for name, cls in structs.items():
+        lines.append(f'    printf("{name} sizeof %zu\\n", sizeof({name}));')
+        for field, _ in cls._fields_:
+            lines.append(f'    printf("{name} {field} %zu %zu\\n", offsetof({name}, {field}), '
+                         f'sizeof((({name}*)0)->{field}));')
+    lines += ["    return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    for line in filter(None, out):
+        parts = line.split()
+        cls = structs[parts[0]]
+        if parts[1] == "sizeof":
+            assert int(parts[2]) == ctypes.sizeof(cls), line
+        else:
+            desc = getattr(cls, parts[1])
+            assert (desc.offset, desc.size) == (int(parts[2]), int(parts[3])), line

@@ -7,6 +7,7 @@ import torch
 
 import workloads
 from oracle import batch as ref_batch, step as ref_step
+from tests.gpu_helpers import read_rows_i32
 
 pytestmark = pytest.mark.gpu
 
@@ -88,6 +89,19 @@ def test_groups_compile_tables_and_condense(rt):
         torch.cuda.synchronize()
         exp = ref_step.padded_block_table(rows, width, -1, ratio, blocks_of=lambda i, r: ref.rows[i].group_blocks[group])
         assert np.array_equal(dst.cpu().numpy(), np.asarray(exp, np.int32)), (group, ratio)
+
+    # the persistent per-group tables through the column views
+    cols = ric.ric_get_columns(b.h)
+    assert cols.group_blocks[0] == cols.blocks and cols.group_block_stride[0] == cols.block_stride
+    assert cols.group_blocks[3] is None and cols.group_block_stride[3] == 0
+    for group in (1, 2):
+        counts = ric.ric_read_device(cols.group_num_blocks[group], 4 * len(order), np.int32)
+        for i in range(len(order)):
+            want_ids = ref.rows[i].group_blocks[group]
+            assert counts[i] == len(want_ids), (group, i)
+            got_ids = read_rows_i32(b.workspace, cols.group_blocks[group], cols.group_block_stride[group], [i],
+                                    len(want_ids))[0]
+            assert list(got_ids) == list(want_ids), (group, i)
 
     # a row whose second table does not cover its positions is rejected
     rid0 = order[0]
