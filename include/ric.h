@@ -277,9 +277,9 @@ int ric_spec_decode_metadata(ric_batch* b, const int32_t* num_draft_tokens, ric_
  * Entries past a row's own (expanded) blocks are set to `fill` (nano-vllm pads
  * with -1, [P5 prepare_block_tables]).  dst: DEVICE int32[R][width],
  * width <= k * the group's table capacity, and k * the group's pool size must
- * stay below 2^31 (expanded ids are int32).  The persistent table itself
- * (ric_get_columns, group 0) can be used directly when stale entries past
- * each row's count are acceptable.  Errors: ESTATE (no schedule since the
+ * stay below 2^31 (expanded ids are int32).  The persistent tables themselves
+ * (ric_get_columns: group_blocks[g]) can be used directly when stale entries
+ * past each row's count are acceptable.  Errors: ESTATE (no schedule since the
  * last row change), EINVAL. */
 int ric_block_table_padded(ric_batch* b, int32_t group, int32_t kernel_blocks_per_block, int32_t width,
                            int32_t fill, int32_t* dst);
