@@ -8,6 +8,7 @@ only sequences the calls: load the request history into the persistent batch
 layer, gather hidden rows."""
 from __future__ import annotations
 
+import os
 from dataclasses import dataclass
 from typing import List, Optional
 
@@ -17,6 +18,7 @@ import torch
 from . import _ric as ric
 
 _TORCH_DT = {"f16": torch.float16, "bf16": torch.bfloat16}
+DEBUG = os.environ.get("RIC_DEBUG", "") not in ("", "0")
 
 
 def config_of(w) -> ric.ric_config:
@@ -84,7 +86,30 @@ class Batch:
         ric.ric_schedule(self.h, [by_id[i].num_computed for i in order], [by_id[i].num_scheduled for i in order])
 
     def compile(self, n_pad: int) -> ric.ric_step:
-        return ric.ric_compile(self.h, n_pad)
+        s = ric.ric_compile(self.h, n_pad)
+        if DEBUG:
+            self.debug_dump(s)
+        return s
+
+    def debug_dump(self, s: ric.ric_step, limit: int = 32) -> None:
+        """Print the small per-step arrays a developer checks first when a step
+        goes wrong (request order, counts, boundaries, positions, slots,
+        logits rows, discard), not the tables.  Synchronises: debugging only,
+        enabled by RIC_DEBUG=1."""
+        R, n = s.num_reqs, s.num_tokens_padded
+        cols = ric.ric_get_columns(self.h)
+        show = lambda a: " ".join(str(int(x)) for x in a[:limit]) + (" ..." if len(a) > limit else "")
+        print(f"[ric] R={R} N={s.num_actual_tokens} N_pad={n} max_q={s.max_query_len} "
+              f"max_seq={s.max_seq_len} sampled={s.num_sampled}")
+        print(f"[ric] req_ids    {show(self.row_order())}")
+        print(f"[ric] computed   {show(self.device_i32(cols.num_computed, R))}")
+        print(f"[ric] scheduled  {show(self.device_i32(cols.num_scheduled, R))}")
+        print(f"[ric] qsl        {show(self.device_i32(s.query_start_loc, R + 1))}")
+        print(f"[ric] positions  {show(self.device_i32(s.positions, n))}")
+        print(f"[ric] seq_lens   {show(self.device_i32(s.seq_lens, R))}")
+        print(f"[ric] slots      {show(self.device_i32(s.slot_mapping, n))}")
+        print(f"[ric] logits     {show(self.device_i32(s.logits_indices, R))}")
+        print(f"[ric] discard    {show(self.device_u8(s.discard, R))}", flush=True)
 
     # inspection (tests) ------------------------------------------------------
     def device_i32(self, ptr: int, n: int) -> np.ndarray:

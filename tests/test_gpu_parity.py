@@ -623,3 +623,17 @@ def test_c_program_through_the_abi(rt, tmp_path):
     for t, s in enumerate(g["slot_mapping"]):
         assert first[s] == t + 1
     assert all(first[i] == 0 for i in range(4, len(first)) if i not in g["slot_mapping"])
+
+
+def test_debug_dump_prints_the_step(rt, capsys):
+    """RIC_DEBUG's dump shows the small per-step arrays of the worked example."""
+    w = workloads.get("worked_example")
+    b, s, ref, order, exp, _ = _compile(rt, w)
+    b.debug_dump(s)
+    out = capsys.readouterr().out
+    assert "[ric] R=3 N=20 N_pad=32" in out
+    assert "[ric] qsl        0 7 8 20\n" in out
+    assert "[ric] seq_lens   7 6 22\n" in out
+    assert "[ric] logits     6 7 19\n" in out
+    assert "[ric] positions  0 1 2 3 4 5 6 5 10 11" in out
+    b.close()
