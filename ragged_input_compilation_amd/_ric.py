@@ -12,7 +12,9 @@ import os
 
 import numpy as np
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libric.so")
+# RIC_LIBRARY may name another build of the same library (tests load a
+# host-only build through it); by default the in-tree libric.so.
+LIB_PATH = os.environ.get("RIC_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libric.so")
 
 RIC_OK, RIC_EINVAL, RIC_ENOMEM, RIC_EFULL, RIC_ENOENT, RIC_EEXIST, RIC_ERANGE, RIC_EHIP, RIC_ESTATE = \
     0, -1, -2, -3, -4, -5, -6, -7, -8

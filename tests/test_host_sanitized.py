@@ -1,0 +1,169 @@
+"""The library's host control plane (ric_host.cpp) under AddressSanitizer and
+UndefinedBehaviorSanitizer, on the CPU: it is built with g++ together with a
+test double for the device (tests/host_fake/fake_device.cpp: "device" memory
+is host memory; only the column-store kernels act), loaded through the normal
+binding, and driven through a seeded random sequence of adds, removals,
+token and block appends, block replacements (two KV-cache groups), condense,
+sampled-token appends, schedules and compiles, with a staging log small
+enough to force split uploads.  After every flush the column store equals the
+reference batch.  Any out-of-bounds access or undefined behaviour aborts."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+_CHILD = r"""
+import ctypes, sys
+import numpy as np
+sys.path.insert(0, {root!r})
+from ragged_input_compilation_amd import _ric as ric
+from oracle.batch import RefBatch
+
+MR, M, MB, POOL, B = 24, 96, 24, 60000, 4
+GB1 = 8                          # group 1 block size (its table holds M / GB1 entries)
+cfg = ric.make_config(max_num_reqs=MR, max_model_len=M, block_size=B, max_blocks_per_req=MB,
+                      max_num_batched_tokens=256, num_kv_blocks=POOL, null_block=0,
+                      staging_bytes=2 * 12 * MR * 4 + (64 << 10), num_kv_groups=2,
+                      group_block_size=[0, GB1], group_num_kv_blocks=[0, POOL], group_slot_mode=[0, 0])
+h = ric.ric_create(cfg, 0)
+ref = RefBatch(MR, M, MB, POOL)
+rng = np.random.default_rng(17)
+free = list(rng.permutation(np.arange(1, POOL)))
+next_id = 0
+
+def words(ptr, n):
+    return np.ctypeslib.as_array((ctypes.c_int32 * max(n, 1)).from_address(ptr))[:n].copy()
+
+def check():
+    ric.ric_flush(h)
+    cols = ric.ric_get_columns(h)
+    for row, r in enumerate(ref.rows):
+        if r is None:
+            continue
+        T = len(r.tokens)
+        assert words(cols.num_tokens + 4 * row, 1)[0] == T, row
+        assert words(cols.num_prompt + 4 * row, 1)[0] == r.num_prompt, row
+        assert words(cols.num_blocks + 4 * row, 1)[0] == len(r.blocks), row
+        assert list(words(cols.tokens + 4 * row * cols.token_stride, T)) == r.tokens, row
+        assert list(words(cols.blocks + 4 * row * cols.block_stride, len(r.blocks))) == r.blocks, row
+        g1 = r.group_blocks.get(1, [])
+        assert words(cols.group_num_blocks[1] + 4 * row, 1)[0] == len(g1), row
+        assert list(words(cols.group_blocks[1] + 4 * row * cols.group_block_stride[1], len(g1))) == g1, row
+        temp = np.ctypeslib.as_array((ctypes.c_float * 1).from_address(cols.temperature + 4 * row))[0]
+        assert temp == np.float32(r.sampling[0]), row
+    assert ric.ric_num_reqs(h) == ref.num_live()
+    for row in range(MR):
+        want = ref.rows[row].req_id if ref.rows[row] is not None else None
+        assert ric.ric_req_at(h, row) == want, row
+
+def take(n):
+    return [int(free.pop()) for _ in range(n)]
+
+for step in range(600):
+    op = rng.integers(0, 9)
+    live = [r.req_id for r in ref.rows if r is not None]
+    if op <= 1 and ref.num_live() < MR:
+        T = int(rng.integers(1, M - 10))
+        toks = rng.integers(0, 1 << 20, T).tolist()
+        blocks = take(-(-T // B))
+        samp = (float(rng.random()), float(rng.random()), 1.0, int(rng.integers(0, 50)))
+        c = int(rng.integers(0, T))
+        ric.ric_add_request(h, next_id, toks, T, c, blocks, samp)
+        ref.add_request(next_id, toks, T, c, blocks, samp)
+        g1 = take(-(-T // GB1))
+        ric.ric_append_blocks_group(h, next_id, 1, g1)
+        ref.append_blocks_group(next_id, 1, g1)
+        next_id += 1
+    elif op in (2, 3) and live:
+        for rid in rng.choice(live, size=int(rng.integers(1, min(4, len(live)) + 1)), replace=False):
+            ric.ric_remove_request(h, int(rid))
+            ref.remove_request(int(rid))
+    elif op == 4 and live:
+        rid = int(rng.choice(live))
+        r = ref.rows[ref.row_of[rid]]
+        n = int(rng.integers(0, min(8, M - len(r.tokens)) + 1))
+        ids = rng.integers(0, 1 << 20, n).tolist()
+        ric.ric_append_tokens(h, rid, ids)
+        ref.append_tokens(rid, ids)
+        need = -(-len(r.tokens) // B) - len(r.blocks)
+        if need > 0:
+            more = take(need)
+            ric.ric_append_blocks(h, rid, more)
+            ref.append_blocks(rid, more)
+        need1 = -(-len(r.tokens) // GB1) - len(r.group_blocks.get(1, []))
+        if need1 > 0:
+            more = take(need1)
+            ric.ric_append_blocks_group(h, rid, 1, more)
+            ref.append_blocks_group(rid, 1, more)
+    elif op == 5 and live:
+        rid = int(rng.choice(live))
+        r = ref.rows[ref.row_of[rid]]
+        ids = take(len(r.blocks))
+        ric.ric_replace_blocks(h, rid, ids)
+        ref.replace_blocks(rid, ids)
+        ids1 = take(len(r.group_blocks.get(1, [])))
+        ric.ric_replace_blocks_group(h, rid, 1, ids1)
+        ref.replace_blocks_group(rid, 1, ids1)
+    elif op == 6:
+        assert ric.ric_condense(h) == len(ref.condense())
+        check()
+    elif op == 7 and live:
+        ric.ric_condense(h)
+        ref.condense()
+        rows = [i for i, r in enumerate(ref.rows) if r is not None and len(r.tokens) < M
+                and -(-(len(r.tokens) + 1) // B) <= len(r.blocks) and -(-(len(r.tokens) + 1) // GB1)
+                <= len(r.group_blocks.get(1, []))]
+        if rows:
+            sampled = np.asarray(rng.integers(0, 1 << 20, len(rows)), np.int32)
+            src = list(rng.permutation(len(rows)))
+            ric.ric_append_sampled(h, rows, sampled.ctypes.data, len(rows), src)
+            for k, row in enumerate(rows):
+                ref.rows[row].tokens.append(int(sampled[src[k]]))
+        check()
+    elif op == 8 and live:
+        ric.ric_condense(h)
+        ref.condense()
+        R = ref.num_live()
+        c, q = [], []
+        for i in range(R):
+            r = ref.rows[i]
+            T = len(r.tokens)
+            ci = int(rng.integers(0, T))
+            qi = int(rng.integers(1, T - ci + 1))
+            c.append(ci)
+            q.append(qi)
+        if sum(q) <= 256:
+            ric.ric_schedule(h, c, q)
+            ref.schedule(c, q)
+            s = ric.ric_compile(h, sum(q))
+            assert (s.num_reqs, s.num_actual_tokens) == (R, sum(q))
+            d = [min(x - 1, 2) for x in q]
+            m = ric.ric_spec_decode_metadata(h, d)
+            assert m.num_logits == sum(d) + R
+            check()
+check()
+ric.ric_destroy(h)
+print("sanitized control plane ok", next_id)
+"""
+
+
+def test_host_control_plane_under_asan_and_ubsan(tmp_path):
+    asan = subprocess.run(["gcc", "-print-file-name=libasan.so"], capture_output=True, text=True).stdout.strip()
+    if not os.path.isabs(asan) or not os.path.exists(asan):
+        pytest.skip("no AddressSanitizer runtime for gcc here")
+    so = tmp_path / "libric_fake_device.so"
+    subprocess.run(["g++", "-std=c++17", "-O1", "-g", "-fPIC", "-shared", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-D__HIP_PLATFORM_AMD__",
+                    "-I", "/opt/rocm/include", "-I", os.path.join(ROOT, "include"),
+                    os.path.join(ROOT, "ragged_input_compilation_amd", "csrc", "ric_host.cpp"),
+                    os.path.join(ROOT, "tests", "host_fake", "fake_device.cpp"), "-o", str(so)], check=True)
+    env = {**os.environ, "LD_PRELOAD": asan, "ASAN_OPTIONS": "detect_leaks=0:abort_on_error=1",
+           "RIC_LIBRARY": str(so)}
+    child = subprocess.run([sys.executable, "-c", _CHILD.format(root=ROOT)], capture_output=True, text=True,
+                           timeout=600, env=env)
+    assert child.returncode == 0, child.stdout[-2000:] + child.stderr[-4000:]
+    assert "sanitized control plane ok" in child.stdout
+    assert "AddressSanitizer" not in child.stderr and "runtime error" not in child.stderr
