@@ -28,8 +28,6 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 KV_EVENT_EVERY = 8      # timed steps carrying events around the K/V launch: 1 in 8 (each pair perturbs its step)
-KV_LONG_RUN_TOKENS = 64  # mean scheduled tokens per request from which the K/V hint is set ...
-KV_LONG_RUN_BYTES = 256 << 20   # ... in a launch that moves at least this many bytes
 METRIC = "scheduled tokens/sec per step (compile + KV write); achieved HBM GB/s vs peak"
 DESCRIPTIONS = {
     "worked_example": "3 requests (prefill 7, decode 5+1, chunk 10..21), N=20 padded to 32, block 16, "
@@ -78,11 +76,12 @@ def step_bytes(w):
                 total=compile_b + kv_b + gather_b)
 
 
-def kv_kernel_name(w, n_tokens):
-    """Which K/V launch shape the library picks for this size (mirrors its
-    launcher: wave rows for <= 2048 tokens of 1/2/4 KiB rows, else chunk tiles)."""
+def kv_kernel_name(w, n_tokens, flags=0):
+    """Which K/V launch shape the library picks (mirrors its launcher: without
+    the cached-sources hint, wave rows for <= 8192 tokens of 1/2/4 KiB rows;
+    otherwise chunk tiles)."""
     cpl = w.row_bytes // 1024
-    if w.row_bytes % 1024 == 0 and cpl in (1, 2, 4) and n_tokens <= 2048:
+    if not flags and w.row_bytes % 1024 == 0 and cpl in (1, 2, 4) and n_tokens <= 8192:
         return "kv_wave_kernel"
     return "kv_chunk_kernel"
 
@@ -186,11 +185,8 @@ class GpuStep:
         st = ctypes.c_void_p(self.stream or None)
         lib = ric.lib()
         self.lib = lib
-        # the caller knows its step's shape: long prefill chunks write long runs of consecutive slots,
-        # and streaming loads pay off from about 256 MB moved per launch
-        long_runs = self.N >= KV_LONG_RUN_TOKENS * max(len(live), 1)
-        big = 4 * L * self.N * w.row_bytes >= KV_LONG_RUN_BYTES
-        self.kv_flags = ric.RIC_KV_LONG_RUNS if long_runs and big else 0
+        # the timed steps rotate over instances, so the sources come from HBM, not the caches
+        self.kv_flags = 0
         self.kv_args = [ctypes.cast(a, pp) for a in self._ptrs] + [
             L, ctypes.c_void_p(self.step.slot_mapping), self.n_pad, 0, w.row_bytes,
             w.num_kv_blocks * w.block_size, None, self.kv_flags, st]
@@ -344,6 +340,33 @@ def cpu_baseline(w, seconds):
                        f"mmap'd full-size host caches, hidden-row gather)")
 
 
+def kv_sources_cached(ric, torch, sets, nbytes, reps=20):
+    """The K/V launch right after its sources were rewritten in place (x * 1
+    by a torch kernel), so that they sit in the caches as they do when the
+    write follows the K/V projection inside a model: with the cached-sources
+    hint (chunk tiles) and without it (the shape picked for uncached
+    sources)."""
+    out = {}
+    for key, flags in (("us_with_hint", ric.RIC_KV_SOURCES_CACHED), ("us_without_hint", 0)):
+        times = []
+        for i in range(reps + 2):
+            st = sets[i % len(sets)]
+            for t in st.k + st.v:
+                t.mul_(1)
+            args = list(st.kv_args)
+            args[11] = flags
+            a, b = Event(), Event()
+            a.record()
+            st._check(st.lib.ric_reshape_and_cache(*args))
+            b.record()
+            times.append((a, b))
+        torch.cuda.synchronize()
+        out[key] = sorted(a.elapsed_time(b) for a, b in times[2:])[reps // 2] * 1e3
+    out["gbps_with_hint"] = nbytes / (out["us_with_hint"] * 1e-6) / 1e9
+    out["frac_with_hint"] = out["gbps_with_hint"] / HBM_PEAK_GBPS
+    return out
+
+
 def copy_ceiling(ric, torch, sets, w, sb, reps=20):
     """What a plain copy of the K/V launch's bytes reaches on this GPU: torch's
     own device copy (half the bytes read, half written, rotating over buffers
@@ -375,7 +398,7 @@ def copy_ceiling(ric, torch, sets, w, sb, reps=20):
         off = B + k * n_pad if B + (len(sets) + 1) * n_pad <= num_slots else B
         slots.append(torch.arange(off, off + n_pad, dtype=torch.int32, device="cuda"))
     t_ident = math.inf
-    for flags in (0, ric.RIC_KV_LONG_RUNS):   # the faster load variant at this size
+    for flags in (0, ric.RIC_KV_SOURCES_CACHED):   # the faster launch shape at this size
         times = []
         for i in range(reps + 2):
             k = i % len(sets)
@@ -630,6 +653,7 @@ def main():
     ck_warm_ms = bracketed(50, False, True)
     del flush_buf
     ceiling = copy_ceiling(ric, torch, sets, w0, sb)
+    cached = kv_sources_cached(ric, torch, sets, sb["kv"])
     nxt = next_rows(ric, runner, torch, w0, sets[0])
 
     calib = calibrate_copy(ric, torch, runner.current_stream()) if args.calibrate_copy else None
@@ -652,13 +676,14 @@ def main():
         "config": {"workload": f"{args.config}: {DESCRIPTIONS[args.config]}", "num_reqs": sb["R"],
                    "num_tokens": N, "num_layers": w0.num_layers, "rotation_instances": S},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": load_traffic(kv_kernel_name(w0, sb["N"]), args.config),
-                     "kernel": kv_kernel_name(w0, sb["N"]), "kv_flags": sets[0].kv_flags,
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": load_traffic(kv_kernel_name(w0, sets[0].n_pad), args.config),
+                     "kernel": kv_kernel_name(w0, sets[0].n_pad), "kv_flags": sets[0].kv_flags,
                      "bytes_per_launch": sb["kv"],
                      "avg_launch_us": kv_mean * 1e3, "event_samples": len(ev),
                      "frac_of_copy_ceiling": achieved / max(ceiling["torch_copy_gbps"],
                                                             ceiling["identity_slots_gbps"])},
         "copy_ceiling": ceiling,
+        "kv_sources_cached": cached,
         "compile_plus_kv": {"bytes": sb["compile"] + sb["kv"],
                             "warm_us": ck_warm_ms * 1e3,
                             "warm_frac_of_peak": (sb["compile"] + sb["kv"]) / (ck_warm_ms * 1e-3) / 1e9
