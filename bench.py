@@ -76,12 +76,11 @@ def step_bytes(w):
                 total=compile_b + kv_b + gather_b)
 
 
-def kv_kernel_name(w, n_tokens, flags=0):
-    """Which K/V launch shape the library picks (mirrors its launcher: without
-    the cached-sources hint, wave rows for <= 8192 tokens of 1/2/4 KiB rows;
-    otherwise chunk tiles)."""
+def kv_kernel_name(w, n_tokens):
+    """Which K/V launch shape the library picks (mirrors its launcher: wave
+    rows for <= 8192 tokens of 1/2/4 KiB rows, otherwise chunk tiles)."""
     cpl = w.row_bytes // 1024
-    if not flags and w.row_bytes % 1024 == 0 and cpl in (1, 2, 4) and n_tokens <= 8192:
+    if w.row_bytes % 1024 == 0 and cpl in (1, 2, 4) and n_tokens <= 8192:
         return "kv_wave_kernel"
     return "kv_chunk_kernel"
 
@@ -185,7 +184,6 @@ class GpuStep:
         st = ctypes.c_void_p(self.stream or None)
         lib = ric.lib()
         self.lib = lib
-        # the timed steps rotate over instances, so the sources come from HBM, not the caches
         self.kv_flags = 0
         self.kv_args = [ctypes.cast(a, pp) for a in self._ptrs] + [
             L, ctypes.c_void_p(self.step.slot_mapping), self.n_pad, 0, w.row_bytes,
@@ -343,28 +341,21 @@ def cpu_baseline(w, seconds):
 def kv_sources_cached(ric, torch, sets, nbytes, reps=20):
     """The K/V launch right after its sources were rewritten in place (x * 1
     by a torch kernel), so that they sit in the caches as they do when the
-    write follows the K/V projection inside a model: with the cached-sources
-    hint (chunk tiles) and without it (the shape picked for uncached
-    sources)."""
-    out = {}
-    for key, flags in (("us_with_hint", ric.RIC_KV_SOURCES_CACHED), ("us_without_hint", 0)):
-        times = []
-        for i in range(reps + 2):
-            st = sets[i % len(sets)]
-            for t in st.k + st.v:
-                t.mul_(1)
-            args = list(st.kv_args)
-            args[11] = flags
-            a, b = Event(), Event()
-            a.record()
-            st._check(st.lib.ric_reshape_and_cache(*args))
-            b.record()
-            times.append((a, b))
-        torch.cuda.synchronize()
-        out[key] = sorted(a.elapsed_time(b) for a, b in times[2:])[reps // 2] * 1e3
-    out["gbps_with_hint"] = nbytes / (out["us_with_hint"] * 1e-6) / 1e9
-    out["frac_with_hint"] = out["gbps_with_hint"] / HBM_PEAK_GBPS
-    return out
+    write follows the K/V projection inside a model."""
+    times = []
+    for i in range(reps + 2):
+        st = sets[i % len(sets)]
+        for t in st.k + st.v:
+            t.mul_(1)
+        a, b = Event(), Event()
+        a.record()
+        st.kv()
+        b.record()
+        times.append((a, b))
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) for a, b in times[2:])[reps // 2] * 1e3
+    gbps = nbytes / (us * 1e-6) / 1e9
+    return dict(us=us, gbps=gbps, frac=gbps / HBM_PEAK_GBPS)
 
 
 def copy_ceiling(ric, torch, sets, w, sb, reps=20):
@@ -397,21 +388,18 @@ def copy_ceiling(ric, torch, sets, w, sb, reps=20):
     for k, st in enumerate(sets):
         off = B + k * n_pad if B + (len(sets) + 1) * n_pad <= num_slots else B
         slots.append(torch.arange(off, off + n_pad, dtype=torch.int32, device="cuda"))
-    t_ident = math.inf
-    for flags in (0, ric.RIC_KV_SOURCES_CACHED):   # the faster launch shape at this size
-        times = []
-        for i in range(reps + 2):
-            k = i % len(sets)
-            args = list(sets[k].kv_args)
-            args[5] = ctypes.c_void_p(slots[k].data_ptr())
-            args[11] = flags
-            a, b = Event(), Event()
-            a.record()
-            sets[k]._check(sets[k].lib.ric_reshape_and_cache(*args))
-            b.record()
-            times.append((a, b))
-        torch.cuda.synchronize()
-        t_ident = min(t_ident, sorted(a.elapsed_time(b) for a, b in times[2:])[reps // 2])
+    times = []
+    for i in range(reps + 2):
+        k = i % len(sets)
+        args = list(sets[k].kv_args)
+        args[5] = ctypes.c_void_p(slots[k].data_ptr())
+        a, b = Event(), Event()
+        a.record()
+        sets[k]._check(sets[k].lib.ric_reshape_and_cache(*args))
+        b.record()
+        times.append((a, b))
+    torch.cuda.synchronize()
+    t_ident = sorted(a.elapsed_time(b) for a, b in times[2:])[reps // 2]
     return dict(bytes=sb["kv"], torch_copy_us=t_torch * 1e3, torch_copy_gbps=2 * half / (t_torch * 1e-3) / 1e9,
                 identity_slots_us=t_ident * 1e3, identity_slots_gbps=sb["kv"] / (t_ident * 1e-3) / 1e9)
 

@@ -332,19 +332,11 @@ int ric_compile(ric_batch* b, int32_t num_tokens_padded, ric_step* out);
  *                     src_row_stride and every pointer 16-byte aligned
  *   dev_status        optional DEVICE int32: incremented once per row whose
  *                     slot is outside [0, num_slots) (that row is not written)
- *   flags             0, or RIC_KV_SOURCES_CACHED: a performance hint that
- *                     the source rows were just written (typically by the
- *                     K/V projection right before this call) and are still
- *                     in the device caches.  It selects the chunk-tile shape
- *                     at every size, measured fastest with cached sources;
- *                     without it launches of up to 8192 tokens with 1, 2 or
- *                     4 KiB rows take the wave-per-row shape, fastest when
- *                     the sources come from HBM.  Results are identical
- *                     either way.
+ *   flags             reserved for launch hints; pass 0 (anything else is
+ *                     EINVAL)
  * Up to 32 layers are written by one launch (more layers: one launch per 32).
  * num_tokens <= 2^24 per call.
  * Errors: EINVAL (alignment, counts, unknown flags), EHIP. */
-#define RIC_KV_SOURCES_CACHED 1u
 int ric_reshape_and_cache(const void* const* k, const void* const* v, void* const* k_cache,
                           void* const* v_cache, int32_t num_layers, const int32_t* slot_mapping,
                           int32_t num_tokens, int64_t src_row_stride, int32_t row_bytes,

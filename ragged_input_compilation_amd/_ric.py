@@ -33,7 +33,6 @@ class RicError(RuntimeError):
 
 
 RIC_MAX_KV_GROUPS, RIC_SLOTS_PER_TOKEN, RIC_SLOTS_NONE = 4, 0, 1
-RIC_KV_SOURCES_CACHED = 1
 
 
 class ric_config(ctypes.Structure):

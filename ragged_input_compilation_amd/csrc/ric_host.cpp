@@ -1027,7 +1027,7 @@ int ric_reshape_and_cache(const void* const* k, const void* const* v, void* cons
                           int64_t src_row_stride, int32_t row_bytes, int64_t num_slots, int32_t* dev_status,
                           uint32_t flags, void* stream) {
     if (num_layers < 0 || num_tokens < 0) return fail(RIC_EINVAL, "negative count");
-    if (flags & ~RIC_KV_SOURCES_CACHED) return fail(RIC_EINVAL, "unknown flags 0x%x", flags);
+    if (flags != 0) return fail(RIC_EINVAL, "flags 0x%x: no flag is defined (pass 0)", flags);
     if (num_layers == 0 || num_tokens == 0) return RIC_OK;
     if (num_tokens > kMaxRowsPerLaunch)
         return fail(RIC_EINVAL, "num_tokens %d above %d per call (the grid counts work-items in 32 bits)",
@@ -1046,7 +1046,6 @@ int ric_reshape_and_cache(const void* const* k, const void* const* v, void* cons
     p.slot = slot_mapping;
     p.src_stride = src_row_stride;
     p.num_slots = num_slots;
-    p.sources_cached = (flags & RIC_KV_SOURCES_CACHED) ? 1 : 0;
     p.status = dev_status;
     p.num_tokens = num_tokens;
     p.row_bytes = row_bytes;

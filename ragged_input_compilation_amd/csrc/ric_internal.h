@@ -110,7 +110,6 @@ struct KVParams {
     int32_t row_bytes;
     int32_t chunk_shift;          // log2(row_bytes / 16) when a power of two, else -1
     int32_t rows_per_wg;
-    int32_t sources_cached;       // caller's hint: the sources were just written (still in the caches)
 };
 
 struct GatherParams {

@@ -249,26 +249,23 @@ hipError_t launch_compile(const CompileParams& p, hipStream_t s) {
 
 // ---------------------------------------------------------------------------
 // Paged K/V write: row t of every K and V source goes to cache row slot[t]
-// ([P1 §3. 物理 KV 槽位]; [P3 §实现]).  Two launch shapes, chosen from
-// measured sweeps on MI355X with sources read from HBM and with sources just
-// rewritten (still in the caches, as when this write follows the K/V
-// projection):
+// ([P1 §3. 物理 KV 槽位]; [P3 §实现]).  Two launch shapes, chosen by size from
+// measured sweeps on MI355X:
 //
-// * chunk tiles: blockIdx.y = 2*layer + (K:0, V:1), blockIdx.x = a run of
-//   rows of about 4 KiB; lanes walk the run's 16-byte chunks in order, so a
-//   source run is read contiguously and each cache row is written
-//   contiguously.  Fastest at every size when the sources are cached, and
-//   for large launches from HBM.  More bytes in flight per lane (2-4 loads
-//   before the stores, bigger tiles, a persistent grid) measured slower.
-// * wave rows: blockIdx.y = layer; each wave owns ROWS consecutive tokens and
-//   copies both the K and the V row of each, so one wave-uniform (scalar)
-//   slot load serves both; 4*ROWS*CPL 16-byte loads per lane are in flight
-//   before any store.  Fastest for launches up to 8192 tokens whose sources
-//   come from HBM.
+// * wave rows (up to 8192 tokens of 1, 2 or 4 KiB): blockIdx.y = layer; each
+//   wave owns ROWS consecutive tokens and copies both the K and the V row of
+//   each, so one wave-uniform (scalar) slot load serves both; 4*ROWS*CPL
+//   16-byte loads per lane are in flight before any store.
+// * chunk tiles (larger launches, other row sizes): blockIdx.y = 2*layer +
+//   (K:0, V:1), blockIdx.x = a run of rows of about 4 KiB; lanes walk the
+//   run's 16-byte chunks in order, so a source run is read contiguously and
+//   each cache row is written contiguously.  More bytes in flight per lane
+//   (2-4 loads before the stores, bigger tiles, a persistent grid) measured
+//   slower.
 //
 // Both use non-temporal loads and stores: every byte is touched once, and
-// streaming accesses measured as fast or faster in every pattern, cached
-// sources or not.
+// streaming accesses measured as fast or faster than plain ones in nearly
+// every pattern, with the sources in HBM or still in the caches.
 //
 // A slot outside [0, num_slots) skips that row and counts it in *status.
 // ---------------------------------------------------------------------------
@@ -363,7 +360,7 @@ __global__ __launch_bounds__(64 * WAVES) void kv_wave_kernel(KVParams p) {
 }
 
 constexpr int kKvTileBytes = 4096;        // chunk tiles: about 4 KiB per workgroup
-constexpr int kKvWaveMaxTokens = 8192;    // wave rows up to this many tokens per launch (uncached sources)
+constexpr int kKvWaveMaxTokens = 8192;    // wave rows up to this many tokens per launch
 constexpr int kKvWaveRows = 4;
 constexpr int kKvWaveWaves = 4;
 
@@ -379,7 +376,7 @@ hipError_t launch_kv_scatter(const KVParams& p_in, int num_layers, hipStream_t s
     if (p.num_tokens == 0 || num_layers == 0) return hipSuccess;
     const int cpl = p.row_bytes / 1024;
     const bool wave_ok = p.row_bytes % 1024 == 0 && (cpl == 1 || cpl == 2 || cpl == 4);
-    if (!p.sources_cached && wave_ok && p.num_tokens <= kKvWaveMaxTokens) {
+    if (wave_ok && p.num_tokens <= kKvWaveMaxTokens) {
         if (cpl == 1) launch_wave<1>(p, num_layers, s);
         else if (cpl == 2) launch_wave<2>(p, num_layers, s);
         else launch_wave<4>(p, num_layers, s);

@@ -190,14 +190,14 @@ def test_header_is_plain_c_and_links_from_c(ric, tmp_path):
 
 def test_launch_size_limits_are_checked_before_any_device_work(ric):
     """Per-call row limits (2^24: the grid's work-item count stays within 32
-    bits) and unknown hint bits are rejected by validation alone, so these
-    calls are safe without a GPU."""
+    bits) and non-zero reserved flags are rejected by validation alone, so
+    these calls are safe without a GPU."""
     big = (1 << 24) + 1
     with pytest.raises(ric.RicError) as e:
         ric.ric_reshape_and_cache([16], [16], [16], [16], 16, big, 64, 1024)
     assert e.value.code == ric.RIC_EINVAL
     with pytest.raises(ric.RicError) as e:
-        ric.ric_reshape_and_cache([16], [16], [16], [16], 16, 4, 64, 1024, flags=4)
+        ric.ric_reshape_and_cache([16], [16], [16], [16], 16, 4, 64, 1024, flags=1)
     assert e.value.code == ric.RIC_EINVAL
     with pytest.raises(ric.RicError) as e:
         ric.ric_gather_rows(16, 64, 4, 16, 0, big, 64, 16)

@@ -137,14 +137,13 @@ def test_kv_write_worked_example_full(rt):
     b.close()
 
 
-@pytest.mark.parametrize("name,flags", [("decode_heavy", 0), ("mixed", 0), ("churn", 0), ("long_context", 0),
-                                        ("decode_heavy", 1), ("mixed", 1)])
-def test_kv_write_full_size_sampled(rt, name, flags):
+@pytest.mark.parametrize("name", ["decode_heavy", "mixed", "churn", "long_context"])
+def test_kv_write_full_size_sampled(rt, name):
     """Full-size caches, every layer of the configuration, one launch: sampled
     real tokens (plus every token of up to 2048) are compared with their source
     rows at the oracle's slot, and sampled slots outside the step keep their
-    sentinel.  The cached-sources hint (flags 1) switches decode-heavy and
-    mixed from the wave-per-row shape to chunk tiles; results are the same."""
+    sentinel.  Decode-heavy and mixed take the wave-per-row shape, churn and
+    long-context chunk tiles."""
     ric, runner = rt
     w = workloads.get(name)
     b, s, ref, order, exp, _ = _compile(rt, w)
@@ -153,7 +152,7 @@ def test_kv_write_full_size_sampled(rt, name, flags):
     k, v = runner.alloc_sources(w, n_pad, seed=w.seed + 17)
     kv = runner.KVSet(k, v, kc, vc, w.row_bytes, w.num_kv_blocks * w.block_size)
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    runner.reshape_and_cache(kv, s.slot_mapping, n_pad, dev_status=status.data_ptr(), flags=flags)
+    runner.reshape_and_cache(kv, s.slot_mapping, n_pad, dev_status=status.data_ptr())
     torch.cuda.synchronize()
     assert int(status.item()) == 0
     rng = np.random.default_rng(5)
@@ -438,7 +437,7 @@ def test_out_of_range_indices_are_reported_not_written(rt):
     assert int(status.item()) == 4
     assert torch.equal(kc1[3], k1[0]) and torch.equal(vc1[7], v1[3])
     assert bool((kc1[others] == -1).all()) and bool((vc1[others] == -1).all())
-    # an unknown hint bit is rejected before anything is launched
+    # the reserved flags must be 0: anything else is rejected before a launch
     with pytest.raises(ric.RicError) as e:
         ric.ric_reshape_and_cache([k.data_ptr()], [v.data_ptr()], [kc.data_ptr()], [vc.data_ptr()],
                                   slot.data_ptr(), 4, row_bytes, nslots, flags=2, stream=runner.current_stream())
