@@ -18,7 +18,10 @@ Sources (web pages; cited by title and section):
 
 Modules:
 
-* ``step``        per-token Python loops: the plain definition (P1, P3).
+* ``step``        per-token Python loops: the plain definition (P1, P3), and
+                  the routines of the next rows (kernel-block expansion, padded
+                  tables, per-group slots, sampled-token append, the correction
+                  of optimistic computed counts, speculative-decoding indices).
 * ``vectorised``  the same outputs from numpy library routines
                   (cumsum / repeat / take), as P2 section 8.3 describes them.
 * ``batch``       the persistent row-compacted batch: add, remove, append,

@@ -220,6 +220,36 @@ def append_sampled(rows_tokens, rows, src_index, sampled):
         rows_tokens[row].append(int(sampled[src_index[k] if src_index is not None else k]))
 
 
+def correct_computed(num_computed, rows_tokens, rows, prev_index, num_draft, num_accepted, sampled=None):
+    """Correct optimistically advanced computed counts (asynchronous
+    speculative decoding, [P1 §投机解码：一条请求一轮可能产生多个决策位置]).
+
+    Last step row ``rows[k]`` fed its last token plus d = num_draft[k] drafts
+    and was then scheduled again as if all d had been accepted, i.e. with its
+    computed count advanced by d + 1.  The sampler, at position
+    p = prev_index[k] of its output, kept v = num_accepted[p] tokens: the
+    accepted drafts and one token of its own.  Only the first v of the d + 1
+    fed positions hold K/V that stays valid, so the count drops by d + 1 - v.
+    With ``sampled`` (one token list per sampler position), the last kept
+    token sampled[p][v - 1] is written into the row's history at the
+    corrected count: it is the row's first input of the new step.  A count v
+    outside [1, d + 1] leaves the row unchanged; the number of such rows is
+    returned.  ``num_computed`` and ``rows_tokens`` are indexed by row and
+    updated in place."""
+    bad = 0
+    for k, row in enumerate(rows):
+        p = prev_index[k]
+        d = num_draft[k]
+        v = int(num_accepted[p])
+        if v < 1 or v > d + 1:
+            bad += 1
+            continue
+        num_computed[row] -= d + 1 - v
+        if sampled is not None:
+            rows_tokens[row][num_computed[row]] = int(sampled[p][v - 1])
+    return bad
+
+
 def gather_rows(src_rows, indices, count: int, zero_row):
     """out[m] = src[indices[m]] for m < count; a negative index yields the zero
     row.  [P2 §8.7 execute_model：完整主流程] (hidden_states[logits_indices]);

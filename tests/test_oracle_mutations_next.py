@@ -1,7 +1,8 @@
 """Planted mistakes in the oracle routines beyond the compile (K/V write, row
 gather, condense, kernel-block expansion, padded tables, per-group slots,
-sampled-token append, speculative-decoding indices): each mutant copy must
-fail a pin that holds for the unmutated oracle.  The pins are values the pages
+sampled-token append, the correction of optimistic computed counts,
+speculative-decoding indices): each mutant copy must fail a pin that holds
+for the unmutated oracle.  The pins are values the pages
 print (golden files), library special cases and invariants written here
 independently of the oracle's code.  Mutations are planted in copies, on the
 CPU."""
@@ -73,6 +74,54 @@ def _pins_step(step):
     toks = {0: [1], 1: [2]}
     step.append_sampled(toks, [1, 0], None, [8, 9])
     _check(toks == {0: [1, 9], 1: [2, 8]}, "append in order")
+
+    # Correction of optimistic counts under asynchronous speculative decoding,
+    # pinned by the synchronous path: a host that knows what the sampler kept
+    # extends the history with the kept tokens itself and sets the count to
+    # the positions whose K/V stays valid (the last committed token and the
+    # accepted drafts).  The corrected asynchronous row (drafts in its history,
+    # one placeholder for the next input, count advanced by d + 1) must agree
+    # on the count and on the history through the new first input.  Rows are
+    # reordered between the steps, so the sampler's order differs from the
+    # rows' (a permutation maps them).
+    for _ in range(200):
+        R = int(rng.integers(1, 6))
+        c0 = [int(rng.integers(0, 20)) for _ in range(R)]
+        d = [int(rng.integers(0, 5)) for _ in range(R)]
+        hist = [[int(x) for x in rng.integers(0, 1000, c0[i] + 1)] for i in range(R)]
+        drafts = [[int(x) for x in rng.integers(1000, 2000, d[i])] for i in range(R)]
+        n_acc = [int(rng.integers(0, d[i] + 1)) for i in range(R)]       # accepted drafts
+        own = [int(rng.integers(2000, 3000)) for _ in range(R)]          # the sampler's own token
+        pos_of = [int(x) for x in rng.permutation(R)]                    # sampler position of row i
+        width = max(d) + 1
+        sampled = [[-1] * width for _ in range(R)]
+        kept_n = [0] * R
+        for i in range(R):
+            kept = drafts[i][:n_acc[i]] + [own[i]]
+            sampled[pos_of[i]][:len(kept)] = kept
+            kept_n[pos_of[i]] = len(kept)
+        sync_hist = [hist[i] + drafts[i][:n_acc[i]] + [own[i]] for i in range(R)]
+        sync_c = [c0[i] + 1 + n_acc[i] for i in range(R)]
+        async_hist = [hist[i] + drafts[i] + [-7] for i in range(R)]
+        async_c = [c0[i] + d[i] + 1 for i in range(R)]
+        order = [int(x) for x in rng.permutation(R)]
+        bad = step.correct_computed(async_c, async_hist, order, [pos_of[i] for i in order],
+                                    [d[i] for i in order], kept_n, sampled)
+        _check(bad == 0, "correction: no bad counts")
+        for i in range(R):
+            _check(async_c[i] == sync_c[i], "correction: count")
+            _check(async_hist[i][:async_c[i] + 1] == sync_hist[i], "correction: history through the first input")
+        # without sampled tokens only the count moves
+        c_only = [c0[i] + d[i] + 1 for i in range(R)]
+        h_only = [list(h) for h in async_hist]
+        step.correct_computed(c_only, h_only, order, [pos_of[i] for i in order], [d[i] for i in order], kept_n)
+        _check(c_only == sync_c and h_only == async_hist, "correction: count only")
+    # kept counts outside [1, d + 1] leave their rows as they were
+    c = [10, 10, 10]
+    h = [list(range(12)) for _ in range(3)]
+    bad = step.correct_computed(c, h, [0, 1, 2], [0, 1, 2], [2, 2, 2], [0, 4, 3], [[5, 6, 7, 8]] * 3)
+    _check(bad == 2 and c == [10, 10, 10], "correction: out-of-range counts")
+    _check(h[0] == list(range(12)) and h[1] == list(range(12)) and h[2][10] == 7, "correction: rows untouched")
 
     # Spec decode: no drafts reduces to the printed closed form; with drafts,
     # invariants stated independently.
@@ -166,6 +215,16 @@ STEP_MUTANTS = [
     ("drafts.append(int(input_ids[end - d + k]))", "drafts.append(int(input_ids[end - d + k - 1]))"),
     ("bonus.append(cu[-1] - 1)", "bonus.append(cu[-1])"),
     ("cu.append(cu[-1] + d + 1)", "cu.append(cu[-1] + d)"),
+    ("num_computed[row] -= d + 1 - v", "num_computed[row] -= d - v"),                 # off by one
+    ("v = int(num_accepted[p])", "v = int(num_accepted[k])"),                         # map ignored
+    ("rows_tokens[row][num_computed[row]] = int(sampled[p][v - 1])",
+     "rows_tokens[row][num_computed[row]] = int(sampled[k][v - 1])"),                 # map ignored
+    ("rows_tokens[row][num_computed[row]] = int(sampled[p][v - 1])",
+     "rows_tokens[row][num_computed[row] + 1] = int(sampled[p][v - 1])"),             # wrong position
+    ("rows_tokens[row][num_computed[row]] = int(sampled[p][v - 1])",
+     "rows_tokens[row][num_computed[row]] = int(sampled[p][0])"),                     # first, not last kept
+    ("if v < 1 or v > d + 1:", "if v < 1 or v > d + 2:"),                             # bound off by one
+    ("if v < 1 or v > d + 1:", "if v > d + 1:"),                                      # lower bound dropped
 ]
 
 BATCH_MUTANTS = [
