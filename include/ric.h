@@ -203,6 +203,13 @@ int ric_remove_request(ric_batch* b, uint64_t req_id, int32_t* out_row);
 /* Append new token ids to the request's history.  Errors: ENOENT, EFULL. */
 int ric_append_tokens(ric_batch* b, uint64_t req_id, const int32_t* ids, int32_t n);
 
+/* Keep the first num_tokens of the request's history, dropping the rest
+ * (drafts that verification rejected: only the verified prefix is committed,
+ * [P1 §投机解码：一条请求一轮可能产生多个决策位置]).  Only the count changes;
+ * the dropped entries are overwritten by later appends.  Errors: ENOENT,
+ * ERANGE (num_tokens below the prompt length or above the history). */
+int ric_truncate_tokens(ric_batch* b, uint64_t req_id, int32_t num_tokens);
+
 /* Append newly allocated block ids to the request's block-table row.
  * Errors: ENOENT, EFULL, ERANGE (bad block id). */
 int ric_append_blocks(ric_batch* b, uint64_t req_id, const int32_t* ids, int32_t n);
@@ -268,6 +275,41 @@ typedef struct {
  * draft counts num_draft_tokens[R].  Errors: ESTATE (no compile of the current
  * schedule), EINVAL (d_i < 0 or d_i + 1 > q_i). */
 int ric_spec_decode_metadata(ric_batch* b, const int32_t* num_draft_tokens, ric_spec_decode* out);
+
+/* Correct this step's computed counts on the device when they were scheduled
+ * optimistically (asynchronous speculative decoding, [P1 §投机解码：一条请求一轮
+ * 可能产生多个决策位置]).  Last step row rows[k] fed its last token plus
+ * d = num_draft[k] drafts, and ric_schedule was given its count advanced by
+ * d + 1, as if every draft had been accepted.  The sampler kept
+ * v = dev_num_accepted[p] tokens for it (the accepted drafts plus one of its
+ * own), p = prev_index[k] being the row's position in the sampler's output, so
+ * only v of those d + 1 positions hold valid K/V.  On the device, before the
+ * compile reads it:
+ *     c <- c - (d + 1 - v)
+ * and, when dev_sampled is given, dev_sampled[p * sampled_stride + v - 1] (the
+ * last kept token, the row's first input of this step) is written into the
+ * row's token history at the corrected c.  The host never sees v: positions,
+ * seq_lens, slot mappings, discard, cu_seqlens_k and the device scalars of the
+ * next ric_compile follow the corrected counts with no device-to-host copy.
+ *   rows, prev_index, num_draft  HOST int32[n]; rows distinct, in [0, R)
+ *   dev_num_accepted  DEVICE int32[prev_len], ready on the handle's stream
+ *   dev_sampled       DEVICE int32[prev_len][sampled_stride] or NULL;
+ *                     sampled_stride >= d + 1 for every listed row
+ *   dev_status        optional DEVICE int32: incremented once per row whose v
+ *                     lies outside [1, d + 1]; that row keeps its count and
+ *                     gets no token
+ * Call it after ric_schedule and before ric_compile, at most once per
+ * schedule.  The host mirror keeps the scheduled counts: every check made on
+ * them still holds for the lower corrected counts, and ric_step's host
+ * max_seq_len and num_sampled are computed from them (an upper bound, and the
+ * count before correction); dev_scalars hold the corrected values.  The
+ * caller passes the corrected counts to its next ric_schedule once it knows
+ * them.  Errors: ESTATE (no schedule, already compiled or corrected), EINVAL
+ * (row not scheduled or repeated, position outside [0, prev_len), d < 0 or
+ * d above the row's scheduled count, sampled_stride too small). */
+int ric_correct_computed(ric_batch* b, int32_t n, const int32_t* rows, const int32_t* prev_index,
+                         const int32_t* num_draft, const int32_t* dev_num_accepted, int32_t prev_len,
+                         const int32_t* dev_sampled, int64_t sampled_stride, int32_t* dev_status);
 
 /* Dense block table of KV-cache group `group` for an attention call that
  * wants one: rows 0..R-1 of the scheduled batch, `width` entries each.

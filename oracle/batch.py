@@ -129,6 +129,15 @@ class RefBatch:
             raise BatchError("token row full")
         r.tokens.extend(int(t) for t in ids)
 
+    def truncate_tokens(self, req_id: int, num_tokens: int) -> None:
+        """Keep the first num_tokens of the history: drafts that verification
+        rejected leave it, since only the verified prefix is committed
+        ([P1 §投机解码：一条请求一轮可能产生多个决策位置]).  The prompt stays."""
+        r = self.rows[self.row_of[req_id]]
+        if num_tokens < r.num_prompt or num_tokens > len(r.tokens):
+            raise BatchError("truncation outside [num_prompt, num_tokens]")
+        del r.tokens[num_tokens:]
+
     def condense_pairs(self) -> List[Tuple[int, int]]:
         """(hole, source) pairs: k-th lowest hole <- k-th highest live row,
         while the hole is below the row."""

@@ -99,6 +99,9 @@ def _load():
         "ric_append_blocks_group": (ctypes.c_int, [_vp, ctypes.c_uint64, ctypes.c_int32, _i32p, ctypes.c_int32]),
         "ric_replace_blocks_group": (ctypes.c_int, [_vp, ctypes.c_uint64, ctypes.c_int32, _i32p, ctypes.c_int32]),
         "ric_spec_decode_metadata": (ctypes.c_int, [_vp, _i32p, ctypes.POINTER(ric_spec_decode)]),
+        "ric_truncate_tokens": (ctypes.c_int, [_vp, ctypes.c_uint64, ctypes.c_int32]),
+        "ric_correct_computed": (ctypes.c_int, [_vp, ctypes.c_int32, _i32p, _i32p, _i32p, _vp, ctypes.c_int32,
+                                                 _vp, ctypes.c_int64, _vp]),
         "ric_num_reqs": (ctypes.c_int32, [_vp]),
         "ric_row_of": (ctypes.c_int32, [_vp, ctypes.c_uint64]),
         "ric_req_at": (ctypes.c_int, [_vp, ctypes.c_int32, ctypes.POINTER(ctypes.c_uint64)]),
@@ -244,6 +247,21 @@ def ric_spec_decode_metadata(h: int, num_draft_tokens) -> ric_spec_decode:
     out = ric_spec_decode()
     _err(_lib.ric_spec_decode_metadata(_vp(h), dp, ctypes.byref(out)))
     return out
+
+
+def ric_truncate_tokens(h: int, req_id: int, num_tokens: int) -> None:
+    _err(_lib.ric_truncate_tokens(_vp(h), req_id, num_tokens))
+
+
+def ric_correct_computed(h: int, rows, prev_index, num_draft, dev_num_accepted: int, prev_len: int,
+                         dev_sampled: int = 0, sampled_stride: int = 0, dev_status: int = 0) -> None:
+    r, rp = _i32(rows)
+    p, pp = _i32(prev_index)
+    d, dp = _i32(num_draft)
+    if not (r.shape == p.shape == d.shape):
+        raise ValueError("rows, prev_index and num_draft differ in length")
+    _err(_lib.ric_correct_computed(_vp(h), r.shape[0], rp, pp, dp, _vp(dev_num_accepted or None), prev_len,
+                                   _vp(dev_sampled or None), sampled_stride, _vp(dev_status or None)))
 
 
 def ric_block_table_padded(h: int, width: int, fill: int, dst: int, group: int = 0,

@@ -69,7 +69,7 @@ struct Layout {
     size_t off_tok, off_blk, off_scal, off_ids, off_pos, off_req, off_slot, off_qsl, off_seq,
         off_logits, off_sample, off_discard, off_dscal, off_pairs, off_cuk, off_samp_off, off_samp_idx,
         off_spec_logits, off_spec_target, off_spec_draft, off_spec_cu, off_spec_bonus, off_spec_d,
-        off_staging, total;
+        off_corr, off_staging, total;
     size_t staging_bytes;
     // KV-cache groups 1..groups-1 (index g): block tables and slot outputs
     int groups;
@@ -133,6 +133,7 @@ Layout layout_of(const ric_config& c) {
     L.off_spec_cu = take((R + 1) * 4);
     L.off_spec_bonus = take(R * 4);
     L.off_spec_d = take(R * 4);
+    L.off_corr = take(R * 3 * 4);
     L.groups = num_groups_of(c);
     for (int g = 1; g < L.groups; ++g) {
         L.xblk_stride[g] = round4(group_cap(c, g));
@@ -194,6 +195,7 @@ struct ric_batch {
     int64_t* d_samp_off = nullptr;
     int32_t *d_spec_logits = nullptr, *d_spec_target = nullptr, *d_spec_draft = nullptr,
             *d_spec_cu = nullptr, *d_spec_bonus = nullptr, *d_spec_d = nullptr;
+    int32_t* d_corr = nullptr;       // [3][max_num_reqs]: rows, sampler positions, draft counts
     uint8_t* d_staging = nullptr;
 
     // pinned delta logs
@@ -218,6 +220,7 @@ struct ric_batch {
     // schedule state
     bool scheduled = false;
     bool compiled = false;           // a compile ran since the last schedule
+    bool corrected = false;          // ric_correct_computed ran since the last schedule
     int32_t sched_R = 0, sched_N = 0, sched_max_q = 0, sched_max_seq = 0, sched_sampled = 0;
 
     int32_t& S(int col, int row) { return scal[(size_t)col * cfg.max_num_reqs + row]; }
@@ -476,6 +479,7 @@ int ric_create(const ric_config* cfg, void* stream, void* workspace, size_t work
     b->d_spec_cu = reinterpret_cast<int32_t*>(b->ws + L.off_spec_cu);
     b->d_spec_bonus = reinterpret_cast<int32_t*>(b->ws + L.off_spec_bonus);
     b->d_spec_d = reinterpret_cast<int32_t*>(b->ws + L.off_spec_d);
+    b->d_corr = reinterpret_cast<int32_t*>(b->ws + L.off_corr);
     b->d_staging = b->ws + L.off_staging;
     for (int i = 0; i < 2; ++i) {
         void* p = nullptr;
@@ -606,6 +610,20 @@ int ric_append_tokens(ric_batch* b, uint64_t req_id, const int32_t* ids, int32_t
     b->S(kNumTokens, row) = T + n;
     b->mark(kNumTokens, row);
     b->pending_epoch[row] = b->epoch;
+    b->scheduled = false;
+    return RIC_OK;
+}
+
+int ric_truncate_tokens(ric_batch* b, uint64_t req_id, int32_t num_tokens) {
+    if (!b) return fail(RIC_EINVAL, "handle is NULL");
+    int32_t row;
+    int rc = find(b, req_id, &row);
+    if (rc) return rc;
+    const int32_t T = b->S(kNumTokens, row), P = b->S(kNumPrompt, row);
+    if (num_tokens < P || num_tokens > T)
+        return fail(RIC_ERANGE, "row %d: %d tokens outside [prompt %d, history %d]", row, num_tokens, P, T);
+    b->S(kNumTokens, row) = num_tokens;
+    b->mark(kNumTokens, row);
     b->scheduled = false;
     return RIC_OK;
 }
@@ -799,6 +817,62 @@ int ric_spec_decode_metadata(ric_batch* b, const int32_t* num_draft_tokens, ric_
     return RIC_OK;
 }
 
+int ric_correct_computed(ric_batch* b, int32_t n, const int32_t* rows, const int32_t* prev_index,
+                         const int32_t* num_draft, const int32_t* dev_num_accepted, int32_t prev_len,
+                         const int32_t* dev_sampled, int64_t sampled_stride, int32_t* dev_status) {
+    if (!b) return fail(RIC_EINVAL, "handle is NULL");
+    DeviceScope ds(b);
+    if (!b->scheduled || b->compiled)
+        return fail(RIC_ESTATE, "needs a schedule that has not been compiled yet");
+    if (b->corrected) return fail(RIC_ESTATE, "this schedule's counts were corrected already");
+    const int32_t R = b->sched_R;
+    if (n < 0 || n > R) return fail(RIC_EINVAL, "n %d outside [0, scheduled rows %d]", n, R);
+    if (n == 0) return RIC_OK;
+    if (!rows || !prev_index || !num_draft || !dev_num_accepted)
+        return fail(RIC_EINVAL, "NULL argument");
+    if (prev_len <= 0) return fail(RIC_EINVAL, "prev_len %d must be positive", prev_len);
+    std::vector<uint8_t> seen((size_t)R, 0);
+    for (int32_t k = 0; k < n; ++k) {
+        const int32_t r = rows[k], d = num_draft[k];
+        if (r < 0 || r >= R) return fail(RIC_EINVAL, "row %d outside the scheduled rows [0, %d)", r, R);
+        if (seen[r]) return fail(RIC_EINVAL, "row %d listed twice", r);
+        seen[r] = 1;
+        if (prev_index[k] < 0 || prev_index[k] >= prev_len)
+            return fail(RIC_EINVAL, "sampler position %d outside [0, %d)", prev_index[k], prev_len);
+        // the correction lowers c by at most d, so the scheduled c must hold d
+        if (d < 0 || d > b->S(kNumComputed, r))
+            return fail(RIC_EINVAL, "row %d: %d drafts, but its scheduled count is %d", r, d,
+                        b->S(kNumComputed, r));
+        if (dev_sampled && sampled_stride < (int64_t)d + 1)
+            return fail(RIC_EINVAL, "sampled_stride %lld cannot hold the %d tokens of row %d", (long long)sampled_stride,
+                        d + 1, r);
+    }
+    const int MR = b->cfg.max_num_reqs;
+    int rc = stage(b, b->d_corr, rows, (size_t)n);
+    if (rc) return rc;
+    rc = stage(b, b->d_corr + MR, prev_index, (size_t)n);
+    if (rc) return rc;
+    rc = stage(b, b->d_corr + 2 * (size_t)MR, num_draft, (size_t)n);
+    if (rc) return rc;
+    rc = flush(b);    // the schedule's counts and these arrays land before the kernel reads them
+    if (rc) return rc;
+    CorrectParams p{};
+    p.computed = b->dcol(kNumComputed);
+    p.tokens = b->d_tok;
+    p.tok_stride = b->L.tok_stride;
+    p.rows = b->d_corr;
+    p.prev = b->d_corr + MR;
+    p.draft = b->d_corr + 2 * (size_t)MR;
+    p.accepted = dev_num_accepted;
+    p.sampled = dev_sampled;
+    p.sampled_stride = sampled_stride;
+    p.status = dev_status;
+    p.n = n;
+    HIP_TRY(launch_correct_computed(p, b->stream));
+    b->corrected = true;
+    return RIC_OK;
+}
+
 int ric_block_table_padded(ric_batch* b, int32_t group, int32_t ratio, int32_t width, int32_t fill, int32_t* dst) {
     if (!b) return fail(RIC_EINVAL, "handle is NULL");
     DeviceScope ds(b);
@@ -941,6 +1015,7 @@ int ric_schedule(ric_batch* b, int32_t R, const int32_t* c, const int32_t* q) {
     }
     b->scheduled = true;
     b->compiled = false;
+    b->corrected = false;
     b->sched_R = R;
     b->sched_N = N;
     b->sched_max_q = mq;

@@ -138,6 +138,20 @@ struct MoveParams {
     int32_t chunk_vec4;           // 16-byte units of token history per workgroup
 };
 
+struct CorrectParams {
+    int32_t* computed;            // device num_computed column
+    int32_t* tokens;              // [max_num_reqs][tok_stride]
+    int64_t tok_stride;
+    const int32_t* rows;          // [n] uploaded: corrected rows
+    const int32_t* prev;          // [n] uploaded: sampler position of each
+    const int32_t* draft;         // [n] uploaded: drafts each verified
+    const int32_t* accepted;      // caller's device array [prev_len]
+    const int32_t* sampled;       // caller's device array [prev_len][sampled_stride], or null
+    int64_t sampled_stride;
+    int32_t* status;              // caller's device counter of out-of-range counts, or null
+    int32_t n;
+};
+
 // Launchers (enqueue only; return the launch status).
 hipError_t launch_compile(const CompileParams& p, hipStream_t s);
 hipError_t launch_kv_scatter(const KVParams& p, int num_layers, hipStream_t s);
@@ -146,6 +160,7 @@ hipError_t launch_move_rows(const MoveParams& p, int max_token_chunks, hipStream
 hipError_t launch_apply_deltas(const uint32_t* payload, const DeltaOp* ops, int n_ops, hipStream_t s);
 hipError_t launch_padded_table(const PaddedTableParams& p, hipStream_t s);
 hipError_t launch_spec_decode(const SpecParams& p, hipStream_t s);
+hipError_t launch_correct_computed(const CorrectParams& p, hipStream_t s);
 // dst_off[k] (int64, in int32 elements of the token table) <- src[src_idx[k]]
 hipError_t launch_append_sampled(int32_t* tokens, const int64_t* dst_off, const int32_t* src_idx,
                                  const int32_t* src, int32_t src_len, int32_t n, int32_t* err, hipStream_t s);

@@ -1,5 +1,7 @@
 // HIP kernels for gfx950 (CDNA4, wave64): step compile, paged K/V write,
-// row gather, condense row move and staged-delta apply.
+// row gather, condense row move, staged-delta apply, and the small kernels of
+// the next rows (padded tables, speculative-decoding indices, sampled-token
+// append, correction of optimistic computed counts).
 //
 // Sources (page title, section):
 //   [P1] "vLLM 源码完全拆解（五）：GPUModelRunner 如何把动态请求拼成一次 GPU 前向"
@@ -598,6 +600,39 @@ hipError_t launch_append_sampled(int32_t* tokens, const int64_t* dst_off, const 
     if (n == 0) return hipSuccess;
     hipLaunchKernelGGL(append_sampled_kernel, dim3((n + 255) / 256), dim3(256), 0, s, tokens, dst_off, src_idx,
                        src, src_len, n, err);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Correction of optimistically advanced computed counts (asynchronous
+// speculative decoding, [P1 §投机解码：一条请求一轮可能产生多个决策位置]).  Row
+// rows[k] was scheduled as if all draft[k] drafts it verified last step were
+// accepted; the sampler kept v = accepted[prev[k]] tokens, so its count drops
+// by draft[k] + 1 - v, on the device, before the compile reads it.  With
+// sampled tokens given, the last kept one becomes the row's token at the
+// corrected count (its first input of this step).  A v outside
+// [1, draft + 1], or a corrected count outside the row, changes nothing and
+// bumps *status.  One thread per row; rows are distinct (checked on the host).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void correct_computed_kernel(CorrectParams p) {
+    const int k = blockIdx.x * 256 + threadIdx.x;
+    if (k >= p.n) return;
+    const int row = p.rows[k];
+    const int pos = p.prev[k];
+    const int d = p.draft[k];
+    const int v = p.accepted[pos];
+    const int c = p.computed[row] - (d + 1 - v);
+    if (v < 1 || v > d + 1 || c < 0 || c >= p.tok_stride) {
+        if (p.status) atomicAdd(p.status, 1);
+        return;
+    }
+    p.computed[row] = c;
+    if (p.sampled) p.tokens[(int64_t)row * p.tok_stride + c] = p.sampled[(int64_t)pos * p.sampled_stride + v - 1];
+}
+
+hipError_t launch_correct_computed(const CorrectParams& p, hipStream_t s) {
+    if (p.n == 0) return hipSuccess;
+    hipLaunchKernelGGL(correct_computed_kernel, dim3((p.n + 255) / 256), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

@@ -8,9 +8,10 @@
 // replaced by host equivalents (allocation, copies, no-op events and
 // synchronisation).  Of the kernel launchers, only those that maintain the
 // column store do their work here (staged-delta apply, condense row move,
-// sampled-token append), so the column store can be compared with the
-// reference batch; the step kernels (compile, K/V write, gather, spec decode,
-// padded tables) are parity-tested on the GPU and do nothing here.
+// sampled-token append, computed-count correction), so the column store can
+// be compared with the reference batch; the step kernels (compile, K/V write,
+// gather, spec decode, padded tables) are parity-tested on the GPU and do
+// nothing here.
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
@@ -104,6 +105,21 @@ hipError_t launch_append_sampled(int32_t* tokens, const int64_t* dst_off, const 
             continue;
         }
         tokens[dst_off[k]] = src[src_idx[k]];
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_correct_computed(const CorrectParams& p, hipStream_t) {
+    for (int k = 0; k < p.n; ++k) {
+        const int row = p.rows[k], pos = p.prev[k], d = p.draft[k];
+        const int v = p.accepted[pos];
+        const int c = p.computed[row] - (d + 1 - v);
+        if (v < 1 || v > d + 1 || c < 0 || c >= p.tok_stride) {
+            if (p.status) ++*p.status;
+            continue;
+        }
+        p.computed[row] = c;
+        if (p.sampled) p.tokens[(int64_t)row * p.tok_stride + c] = p.sampled[(int64_t)pos * p.sampled_stride + v - 1];
     }
     return hipSuccess;
 }

@@ -1,6 +1,8 @@
-"""GPU parity for the rows after the core path: dense padded block tables and
-the device-side append of sampled tokens (async-scheduling input path).
-cu_seqlens_k is compared with every compile in test_gpu_parity.py."""
+"""GPU parity for the rows after the core path: dense padded block tables,
+the device-side append of sampled tokens (async-scheduling input path),
+speculative-decoding indices, and the device-side correction of optimistic
+computed counts (asynchronous speculative decoding).  cu_seqlens_k is compared
+with every compile in test_gpu_parity.py."""
 import numpy as np
 import pytest
 import torch
@@ -157,4 +159,149 @@ def test_spec_decode_metadata(rt, name):
         bad = [r.num_scheduled for r in rows]       # d = q: one too many
         with pytest.raises(ric.RicError):
             ric.ric_spec_decode_metadata(b.h, bad)
+    b.close()
+
+
+def test_async_spec_decode_correction_loop(rt):
+    """Eight rounds of speculative decoding over ten requests.  Each round has
+    a synchronous step (fresh drafts appended, counts known) and then an
+    asynchronous one: the host schedules every row as if all its drafts had
+    been accepted, and ric_correct_computed lowers the counts on the device
+    from an accepted-count array in the sampler's own order, writing the last
+    kept token into the history.  Afterwards the host learns what was kept,
+    drops the rejected drafts (ric_truncate_tokens) and appends the step's new
+    token.  Two requests finish and the batch is condensed midway.  Every
+    compile, the device's computed counts and histories equal the oracle's."""
+    ric, runner = rt
+    rng = np.random.default_rng(33)
+    B, MR, M = 16, 16, 512
+    NB = 4096
+    cfg = ric.make_config(max_num_reqs=MR, max_model_len=M, block_size=B, max_blocks_per_req=M // B,
+                          max_num_batched_tokens=128, num_kv_blocks=NB, null_block=0, staging_bytes=0)
+    b = runner.Batch(cfg)
+    ref = ref_batch.RefBatch(MR, M, M // B, NB)
+    free = list(rng.permutation(np.arange(1, NB)))
+    count = {}                          # request id -> tokens with valid K/V (the last token is the next input)
+    for rid in range(10):
+        T = int(rng.integers(5, 80))
+        toks = rng.integers(0, 50000, T)
+        blks = [int(free.pop()) for _ in range(M // B)]
+        ric.ric_add_request(b.h, rid, toks, T, T - 1, blks)
+        ref.add_request(rid, toks, T, T - 1, blks)
+        count[rid] = T - 1
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def compile_and_compare(tag):
+        order = [rid for rid in ref.req_ids_by_row() if rid is not None]
+        n = sum(ref.rows[i].num_scheduled for i in range(len(order)))
+        want = ref_step.compile_step(ref.step_rows(), block_size=B, max_num_reqs=MR, max_model_len=M,
+                                     max_num_batched_tokens=128, num_kv_blocks=NB, n_pad=n)
+        got = b.step_outputs(b.compile(n))
+        for k in ("input_ids", "positions", "slot_mapping", "seq_lens", "cu_seqlens_k", "query_start_loc",
+                  "logits_indices", "req_indices"):
+            assert np.array_equal(np.asarray(got[k], np.int64), np.asarray(want[k], np.int64)), (tag, k)
+        assert np.array_equal(np.asarray(got["discard"], np.int64), np.asarray(want["discard"], np.int64)), tag
+        assert int(got["dev_scalars"][4]) == max(want["seq_lens"]), tag      # exact max after correction
+        cols = ric.ric_get_columns(b.h)
+        R = len(order)
+        dev_c = ric.ric_read_device(cols.num_computed, 4 * R, np.int32)
+        assert list(dev_c) == [ref.rows[i].num_computed for i in range(R)], tag
+        for i in range(R):
+            T = len(ref.rows[i].tokens)
+            row = ric.ric_read_device(cols.tokens + 4 * i * cols.token_stride, 4 * T, np.int32)
+            assert list(row) == ref.rows[i].tokens, (tag, i)
+
+    for rnd in range(8):
+        if rnd == 4:
+            for rid in (3, 6):
+                ric.ric_remove_request(b.h, rid)
+                ref.remove_request(rid)
+                del count[rid]
+            ric.ric_condense(b.h)
+            ref.condense()
+        order = [rid for rid in ref.req_ids_by_row() if rid is not None]
+        assert b.row_order() == order
+        R = len(order)
+        # synchronous step: the last token plus d fresh drafts
+        d = [int(rng.integers(0, 5)) for _ in range(R)]
+        for i, rid in enumerate(order):
+            drafts = rng.integers(60000, 70000, d[i])
+            ric.ric_append_tokens(b.h, rid, drafts)
+            ref.append_tokens(rid, drafts)
+        c = [count[rid] for rid in order]
+        q = [di + 1 for di in d]
+        ric.ric_schedule(b.h, c, q)
+        ref.schedule(c, q)
+        compile_and_compare((rnd, "sync"))
+        # the sampler keeps v = accepted drafts + 1 tokens per row, reported in its own order
+        pos_of = [int(x) for x in rng.permutation(R)]
+        width = max(d) + 1
+        v = [int(rng.integers(1, di + 2)) for di in d]
+        kept = np.full((R, width), -1, np.int32)
+        acc = np.zeros(R, np.int32)
+        for i, rid in enumerate(order):
+            toks = ref.rows[i].tokens
+            row_kept = toks[c[i] + 1:c[i] + v[i]] + [int(rng.integers(80000, 90000))]
+            kept[pos_of[i], :v[i]] = row_kept
+            acc[pos_of[i]] = v[i]
+        kept_dev = torch.from_numpy(kept).cuda()
+        acc_dev = torch.from_numpy(acc).cuda()
+        # asynchronous step: counts advanced as if every draft was accepted,
+        # one placeholder for the next input, then the device correction
+        for i, rid in enumerate(order):
+            ric.ric_append_tokens(b.h, rid, [-5])
+            ref.append_tokens(rid, [-5])
+        c_opt = [c[i] + d[i] + 1 for i in range(R)]
+        ric.ric_schedule(b.h, c_opt, [1] * R)
+        ref.schedule(c_opt, [1] * R)
+        rows = [int(x) for x in rng.permutation(R)]
+        ric.ric_correct_computed(b.h, rows, [pos_of[i] for i in rows], [d[i] for i in rows], acc_dev.data_ptr(),
+                                 R, kept_dev.data_ptr(), width, status.data_ptr())
+        cc = [ref.rows[i].num_computed for i in range(R)]
+        bad = ref_step.correct_computed(cc, [ref.rows[i].tokens for i in range(R)], rows,
+                                        [pos_of[i] for i in rows], [d[i] for i in rows], acc, kept.tolist())
+        assert bad == 0
+        for i in range(R):
+            ref.rows[i].num_computed = cc[i]
+            assert cc[i] == c[i] + v[i]
+        compile_and_compare((rnd, "async"))
+        # the host learns what was kept: rejected drafts leave the history,
+        # and the async step's own sampled token follows the kept ones
+        for i, rid in enumerate(order):
+            keep = c[i] + v[i] + 1
+            ric.ric_truncate_tokens(b.h, rid, keep)
+            ref.truncate_tokens(rid, keep)
+            y = int(rng.integers(0, 50000))
+            ric.ric_append_tokens(b.h, rid, [y])
+            ref.append_tokens(rid, [y])
+            count[rid] = keep
+    assert int(status.item()) == 0
+
+    # out-of-range kept counts leave their rows alone and are counted
+    order = [rid for rid in ref.req_ids_by_row() if rid is not None]
+    R = len(order)
+    c = [count[rid] for rid in order]
+    ric.ric_schedule(b.h, c, [1] * R)
+    ref.schedule(c, [1] * R)
+    acc_bad = torch.tensor([0, 3, 1] + [1] * (R - 3), dtype=torch.int32, device="cuda")
+    ric.ric_correct_computed(b.h, [0, 1, 2], [0, 1, 2], [1, 1, 0], acc_bad.data_ptr(), R, 0, 0, status.data_ptr())
+    compile_and_compare("bad counts")               # rows 0 and 1 unchanged, row 2 (d = 0, v = 1) unchanged
+    assert int(status.item()) == 2
+    with pytest.raises(ric.RicError) as e:          # after the compile
+        ric.ric_correct_computed(b.h, [0], [0], [0], acc_bad.data_ptr(), R)
+    assert e.value.code == ric.RIC_ESTATE
+    ric.ric_schedule(b.h, c, [1] * R)
+    for args in (([0, 0], [0, 1], [0, 0]),           # row twice
+                 ([0], [R], [0]),                    # position past prev_len
+                 ([0], [0], [c[0] + 1]),             # more drafts than the count holds
+                 ([R], [0], [0])):                   # row not scheduled
+        with pytest.raises(ric.RicError) as e:
+            ric.ric_correct_computed(b.h, *args, acc_bad.data_ptr(), R)
+        assert e.value.code == ric.RIC_EINVAL, args
+    with pytest.raises(ric.RicError) as e:           # stride cannot hold d + 1 tokens
+        ric.ric_correct_computed(b.h, [0], [0], [2], acc_bad.data_ptr(), R, acc_bad.data_ptr(), 2)
+    assert e.value.code == ric.RIC_EINVAL
+    with pytest.raises(ric.RicError) as e:           # into the prompt
+        ric.ric_truncate_tokens(b.h, order[0], ref.rows[0].num_prompt - 1)
+    assert e.value.code == ric.RIC_ERANGE
     b.close()

@@ -4,7 +4,8 @@ test double for the device (tests/host_fake/fake_device.cpp: "device" memory
 is host memory; only the column-store kernels act), loaded through the normal
 binding, and driven through a seeded random sequence of adds, removals,
 token and block appends, block replacements (two KV-cache groups), condense,
-sampled-token appends, schedules and compiles, with a staging log small
+sampled-token appends, schedules, corrections of optimistic computed counts
+and compiles, with a staging log small
 enough to force split uploads.  After every flush the column store equals the
 reference batch.  Any out-of-bounds access or undefined behaviour aborts."""
 import os
@@ -21,6 +22,7 @@ import numpy as np
 sys.path.insert(0, {root!r})
 from ragged_input_compilation_amd import _ric as ric
 from oracle.batch import RefBatch
+from oracle import step as ref_step
 
 MR, M, MB, POOL, B = 24, 96, 24, 60000, 4
 GB1 = 8                          # group 1 block size (its table holds M / GB1 entries)
@@ -33,6 +35,7 @@ ref = RefBatch(MR, M, MB, POOL)
 rng = np.random.default_rng(17)
 free = list(rng.permutation(np.arange(1, POOL)))
 next_id = 0
+corrections = 0
 
 def words(ptr, n):
     return np.ctypeslib.as_array((ctypes.c_int32 * max(n, 1)).from_address(ptr))[:n].copy()
@@ -138,6 +141,33 @@ for step in range(600):
         if sum(q) <= 256:
             ric.ric_schedule(h, c, q)
             ref.schedule(c, q)
+            if rng.random() < 0.5:
+                # optimistic counts corrected from "device" accepted counts
+                n = int(rng.integers(1, R + 1))
+                rows_k = [int(x) for x in rng.choice(R, size=n, replace=False)]
+                d = [int(rng.integers(0, min(c[i], 3) + 1)) for i in rows_k]
+                prev_len = R + 2
+                pos = [int(x) for x in rng.choice(prev_len, size=n, replace=False)]
+                acc = np.asarray(rng.integers(0, 6, prev_len), np.int32)     # some outside [1, d + 1]
+                samp = np.asarray(rng.integers(0, 1 << 20, (prev_len, 4)), np.int32)
+                status = np.zeros(1, np.int32)
+                ric.ric_correct_computed(h, rows_k, pos, d, acc.ctypes.data, prev_len, samp.ctypes.data, 4,
+                                         status.ctypes.data)
+                try:
+                    ric.ric_correct_computed(h, rows_k, pos, d, acc.ctypes.data, prev_len)
+                    raise AssertionError("second correction accepted")
+                except ric.RicError as e:
+                    assert e.code == ric.RIC_ESTATE
+                cc = [ref.rows[i].num_computed for i in range(R)]
+                bad = ref_step.correct_computed(cc, [ref.rows[i].tokens for i in range(R)], rows_k, pos, d, acc,
+                                                samp.tolist())
+                for i in range(R):
+                    ref.rows[i].num_computed = cc[i]
+                ric.ric_flush(h)
+                cols = ric.ric_get_columns(h)
+                assert status[0] == bad
+                assert list(words(cols.num_computed, R)) == cc
+                corrections += 1
             s = ric.ric_compile(h, sum(q))
             assert (s.num_reqs, s.num_actual_tokens) == (R, sum(q))
             d = [min(x - 1, 2) for x in q]
@@ -146,7 +176,7 @@ for step in range(600):
             check()
 check()
 ric.ric_destroy(h)
-print("sanitized control plane ok", next_id)
+print("sanitized control plane ok", next_id, "corrections", corrections)
 """
 
 
@@ -166,4 +196,5 @@ def test_host_control_plane_under_asan_and_ubsan(tmp_path):
                            timeout=600, env=env)
     assert child.returncode == 0, child.stdout[-2000:] + child.stderr[-4000:]
     assert "sanitized control plane ok" in child.stdout
+    assert int(child.stdout.split("corrections")[1]) > 10, child.stdout
     assert "AddressSanitizer" not in child.stderr and "runtime error" not in child.stderr

@@ -153,7 +153,8 @@ def _pins_step(step):
 def _pins_batch(batch):
     """Condense pins: the printed A,B,C,D example and invariants over random
     removal patterns (live rows end exactly [0, R), no request is lost, rows
-    already below R stay put, the k-th hole takes the k-th highest row)."""
+    already below R stay put, the k-th hole takes the k-th highest row); and
+    history truncation as the inverse of an append."""
     g = golden("p1_condense.json")
     b = batch.RefBatch(8, 16, 4, 100)
     for i, name in enumerate(g["rows"]):
@@ -162,6 +163,26 @@ def _pins_batch(batch):
         b.remove_request(name)
     b.condense()
     _check([r.req_id for r in b.rows[:b.num_used_rows()]] == g["expect"]["rows"], "p1 condense")
+
+    # Truncation undoes an append (rejected drafts leave the history), keeps
+    # every other column, refuses to cut into the prompt.
+    b = batch.RefBatch(2, 32, 4, 100)
+    b.add_request(5, [10, 11, 12, 13], 3, 2, [7])
+    b.append_tokens(5, [20, 21, 22])
+    b.truncate_tokens(5, 5)
+    r = b.rows[0]
+    _check(r.tokens == [10, 11, 12, 13, 20], "truncate keeps the prefix")
+    _check((r.num_prompt, r.num_computed, r.blocks) == (3, 2, [7]), "truncate keeps the columns")
+    b.truncate_tokens(5, 5)
+    _check(r.tokens == [10, 11, 12, 13, 20], "truncate to the length is a no-op")
+    b.truncate_tokens(5, 3)
+    _check(r.tokens == [10, 11, 12], "truncate to the prompt")
+    for bad_len in (2, 4):
+        try:
+            b.truncate_tokens(5, bad_len)
+        except batch.BatchError:
+            continue
+        raise AssertionError("truncate outside [prompt, length] accepted")
     rng = np.random.default_rng(9)
     for _ in range(100):
         n = int(rng.integers(1, 20))
@@ -233,6 +254,9 @@ BATCH_MUTANTS = [
     ("            self.rows[l] = None\n", "            pass\n"),                      # source row kept
     ("holes = [i for i in range(used) if self.rows[i] is None]",
      "holes = [i for i in range(used - 1, -1, -1) if self.rows[i] is None]"),         # highest hole first
+    ("del r.tokens[num_tokens:]", "del r.tokens[num_tokens + 1:]"),                   # keeps one too many
+    ("if num_tokens < r.num_prompt or num_tokens > len(r.tokens):",
+     "if num_tokens > len(r.tokens):"),                                               # cuts into the prompt
 ]
 
 
