@@ -412,8 +412,10 @@ def next_rows(ric, runner, torch, w, st, reps=20):
     """Times of the calls beyond the step (untimed diagnostics, events around
     each call; a call that stages host data includes that host work): the
     dense padded block table, the speculative-decoding indices, the device-side
-    append of sampled tokens, and the compile with a second KV-cache group that
-    gets its own slots.  cu_seqlens_k is part of every compile."""
+    append of sampled tokens, the device-side correction of optimistic computed
+    counts, and the compile with a second KV-cache group that gets its own
+    slots.  cu_seqlens_k is part of every compile."""
+    import numpy as np
     median = lambda xs: sorted(xs)[len(xs) // 2]
 
     def timed(fn):
@@ -459,6 +461,36 @@ def next_rows(ric, runner, torch, w, st, reps=20):
     else:
         out["append_sampled"] = dict(rows=0, skipped="no row has room left in its token history")
     b2.close()
+
+    # a step whose scheduled counts are corrected on the device first (every
+    # row verified min(c, 3) drafts, of which the sampler kept none but its
+    # own token), against the same step without the correction
+    b4 = runner.Batch(runner.config_of(w))
+    b4.load_history(w)
+    order4 = b4.row_order()
+    # host arrays built once, as a runner keeps them, so the events time the
+    # library's calls rather than Python list conversion
+    c4 = np.asarray([by_id[i].num_computed for i in order4], np.int32)
+    q4 = np.asarray([by_id[i].num_scheduled for i in order4], np.int32)
+    d4 = np.minimum(c4, 3).astype(np.int32)
+    accepted = torch.ones(R, dtype=torch.int32, device="cuda")
+    kept = torch.randint(0, 1 << 20, (R, 4), dtype=torch.int32, device="cuda")
+    rows4 = np.arange(R, dtype=np.int32)
+
+    def corrected_step():
+        ric.ric_schedule(b4.h, c4, q4)
+        ric.ric_correct_computed(b4.h, rows4, rows4, d4, accepted.data_ptr(), R, kept.data_ptr(), 4)
+        ric.ric_compile(b4.h, st.n_pad)
+
+    def plain_step():
+        ric.ric_schedule(b4.h, c4, q4)
+        ric.ric_compile(b4.h, st.n_pad)
+
+    corrected_step()
+    us_corr, us_plain = timed(corrected_step), timed(plain_step)
+    out["correct_computed"] = dict(rows=R, us_schedule_correct_compile=us_corr, us_schedule_compile=us_plain,
+                                   added_us=us_corr - us_plain, bytes=24 * R)
+    b4.close()
 
     # the compile with a second slotted group (the same block size and ids as
     # group 0), against a batch built the same way with one group
