@@ -573,6 +573,31 @@ def test_non_power_of_two_block_size_at_scale(rt):
     b.close()
 
 
+def test_two_million_token_step(rt):
+    """2^21 scheduled tokens in one compile launch (eight 262144-token chunks
+    at random cached offsets of 524288-token prompts, block size 64: 8192
+    token tiles plus the per-request workgroup), compared in full with the
+    oracle; the histories (16 MiB) reach the device in several staged
+    uploads."""
+    ric, runner = rt
+    rng = np.random.default_rng(15)
+    M, B, Q = 1 << 19, 64, 1 << 18
+    pool = rng.permutation(np.arange(1, 70001)).astype(np.int32)
+    reqs, nxt = [], 0
+    for i in range(8):
+        c = int(rng.integers(0, M - Q + 1))
+        T = M if i % 2 == 0 else c + Q
+        nb = -(-T // B)
+        reqs.append(workloads.Req(i, rng.integers(0, 1 << 20, size=T).astype(np.int32), T, c, Q,
+                                  pool[nxt:nxt + nb]))
+        nxt += nb
+    w = _simple_rows_workload(reqs, B, 8, M, 70001)
+    b, s, ref, order, exp, _ = _compile(rt, w)
+    assert s.num_actual_tokens == 1 << 21
+    assert_step_equal(b.step_outputs(s), exp, "2^21 tokens")
+    b.close()
+
+
 def test_strided_sources_from_a_fused_qkv_tensor(rt):
     """K and V passed as strided views of one [N, Hq+2Hkv, D] projection
     output (row stride larger than the K/V row)."""
