@@ -616,12 +616,19 @@ int ric_append_tokens(ric_batch* b, uint64_t req_id, const int32_t* ids, int32_t
 
 int ric_truncate_tokens(ric_batch* b, uint64_t req_id, int32_t num_tokens) {
     if (!b) return fail(RIC_EINVAL, "handle is NULL");
+    DeviceScope ds(b);
     int32_t row;
     int rc = find(b, req_id, &row);
     if (rc) return rc;
     const int32_t T = b->S(kNumTokens, row), P = b->S(kNumPrompt, row);
     if (num_tokens < P || num_tokens > T)
         return fail(RIC_ERANGE, "row %d: %d tokens outside [prompt %d, history %d]", row, num_tokens, P, T);
+    // A later append lands where a still-staged one may write; the ops of one
+    // flush run in parallel, so the staged writes go first.
+    if (num_tokens < T) {
+        rc = before_row_overwrite(b, row);
+        if (rc) return rc;
+    }
     b->S(kNumTokens, row) = num_tokens;
     b->mark(kNumTokens, row);
     b->scheduled = false;

@@ -15,8 +15,11 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <utility>
+#include <vector>
 
 #include "../../ragged_input_compilation_amd/csrc/ric_internal.h"
 
@@ -75,6 +78,17 @@ const char* hipGetErrorString(hipError_t) { return "fake device"; }
 namespace ric {
 
 hipError_t launch_apply_deltas(const uint32_t* payload, const DeltaOp* ops, int n_ops, hipStream_t) {
+    // The device applies the ops of one flush in parallel, so no two may
+    // write the same bytes: a flush that breaks this aborts the test.
+    std::vector<std::pair<uint64_t, uint64_t>> spans;
+    for (int i = 0; i < n_ops; ++i)
+        if (ops[i].n_words) spans.emplace_back(ops[i].dst, ops[i].dst + 4 * (uint64_t)ops[i].n_words);
+    std::sort(spans.begin(), spans.end());
+    for (size_t i = 1; i < spans.size(); ++i)
+        if (spans[i].first < spans[i - 1].second) {
+            std::fprintf(stderr, "fake device: two staged writes of one flush overlap\n");
+            std::abort();
+        }
     for (int i = 0; i < n_ops; ++i)
         std::memcpy(reinterpret_cast<void*>(ops[i].dst), payload + ops[i].src_word, 4 * (size_t)ops[i].n_words);
     return hipSuccess;

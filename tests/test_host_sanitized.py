@@ -3,7 +3,8 @@ UndefinedBehaviorSanitizer, on the CPU: it is built with g++ together with a
 test double for the device (tests/host_fake/fake_device.cpp: "device" memory
 is host memory; only the column-store kernels act), loaded through the normal
 binding, and driven through a seeded random sequence of adds, removals,
-token and block appends, block replacements (two KV-cache groups), condense,
+token appends and truncations, block appends and replacements (two KV-cache
+groups), condense,
 sampled-token appends, schedules, corrections of optimistic computed counts
 and compiles, with a staging log small
 enough to force split uploads.  After every flush the column store equals the
@@ -91,6 +92,15 @@ for step in range(600):
         ids = rng.integers(0, 1 << 20, n).tolist()
         ric.ric_append_tokens(h, rid, ids)
         ref.append_tokens(rid, ids)
+        if n and rng.random() < 0.5:
+            # drafts rejected: cut back into what was just appended (still
+            # staged) and append other ids over the same positions
+            keep = max(r.num_prompt, len(r.tokens) - int(rng.integers(1, n + 1)))
+            ric.ric_truncate_tokens(h, rid, keep)
+            ref.truncate_tokens(rid, keep)
+            more = rng.integers(0, 1 << 20, int(rng.integers(0, 4))).tolist()
+            ric.ric_append_tokens(h, rid, more)
+            ref.append_tokens(rid, more)
         need = -(-len(r.tokens) // B) - len(r.blocks)
         if need > 0:
             more = take(need)
