@@ -61,18 +61,43 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int* tmp, int* total)
     return off + inc - x;
 }
 
+// Two exclusive scans and two maxima across the workgroup with one barrier:
+// a[0], a[1] are replaced by their exclusive prefix sums (totals in tot[]),
+// m[0], m[1] by the workgroup maxima.  `tmp` holds 4 ints per wave and must
+// not be reused by the caller afterwards.  Every thread must call it.
 template <int NT>
-__device__ __forceinline__ int block_max(int x, int* tmp) {
+__device__ __forceinline__ void block_scan2_max2(int a[2], int m[2], int* tmp, int tot[2]) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = threadIdx.x / kWave;
-    x = wave_max(x);
-    if (lane == 0) tmp[wid] = x;
+    const int inc0 = wave_inclusive_scan(a[0]);
+    const int inc1 = wave_inclusive_scan(a[1]);
+    const int m0 = wave_max(m[0]);
+    const int m1 = wave_max(m[1]);
+    if (lane == kWave - 1) {
+        tmp[4 * wid + 0] = inc0;
+        tmp[4 * wid + 1] = inc1;
+        tmp[4 * wid + 2] = m0;
+        tmp[4 * wid + 3] = m1;
+    }
     __syncthreads();
-    int m = tmp[0];
+    int off0 = 0, off1 = 0, t0 = 0, t1 = 0, mx0 = tmp[2], mx1 = tmp[3];
 #pragma unroll
-    for (int w = 1; w < NT / kWave; ++w) m = max(m, tmp[w]);
-    __syncthreads();
-    return m;
+    for (int w = 0; w < NT / kWave; ++w) {
+        const int v0 = tmp[4 * w + 0];
+        const int v1 = tmp[4 * w + 1];
+        off0 += (w < wid) ? v0 : 0;
+        off1 += (w < wid) ? v1 : 0;
+        t0 += v0;
+        t1 += v1;
+        mx0 = max(mx0, tmp[4 * w + 2]);
+        mx1 = max(mx1, tmp[4 * w + 3]);
+    }
+    a[0] = off0 + inc0 - a[0];
+    a[1] = off1 + inc1 - a[1];
+    tot[0] = t0;
+    tot[1] = t1;
+    m[0] = mx0;
+    m[1] = mx1;
 }
 
 }  // namespace
@@ -95,6 +120,7 @@ __global__ __launch_bounds__(kCompileThreads) void compile_kernel(CompileParams 
     int32_t* s_qsl = smem;               // [R + 1]
     int32_t* s_base = smem + R + 1;      // [R]: c_i - qsl_i, so position = base + t
     int32_t* s_tmp = s_base + R;         // [kCompileThreads / kWave]
+    int32_t* s_red = s_tmp + kCompileThreads / kWave;   // [4 * kCompileThreads / kWave]
 
     const int tid = threadIdx.x;
     const int32_t* col_c = p.scal + (int64_t)kNumComputed * p.max_num_reqs;
@@ -209,12 +235,14 @@ __global__ __launch_bounds__(kCompileThreads) void compile_kernel(CompileParams 
 
     // Per-request outputs (one workgroup).
     const int MR = p.max_num_reqs;
-    int num_sampled = 0, seq_total = 0;
-    int slot_out = block_exclusive_scan<kCompileThreads>(kept, s_tmp, &num_sampled);
-    // key-side boundaries of a varlen attention call: running total of seq_lens
-    int seq_run = block_exclusive_scan<kCompileThreads>(local_seq, s_tmp, &seq_total);
-    max_q = block_max<kCompileThreads>(max_q, s_tmp);
-    max_seq = block_max<kCompileThreads>(max_seq, s_tmp);
+    // compacted-sample positions, and the key-side boundaries of a varlen
+    // attention call (running total of seq_lens), in one pass with the maxima
+    int sc[2] = {kept, local_seq}, mx[2] = {max_q, max_seq}, tot[2];
+    block_scan2_max2<kCompileThreads>(sc, mx, s_red, tot);
+    int slot_out = sc[0], seq_run = sc[1];
+    const int num_sampled = tot[0], seq_total = tot[1];
+    max_q = mx[0];
+    max_seq = mx[1];
     for (int i = r0; i < r1; ++i) {
         const int end = s_qsl[i + 1];
         const int li = end - 1;
@@ -248,7 +276,7 @@ __global__ __launch_bounds__(kCompileThreads) void compile_kernel(CompileParams 
 }
 
 hipError_t launch_compile(const CompileParams& p, hipStream_t s) {
-    const size_t lds = sizeof(int32_t) * (2 * (size_t)p.num_reqs + 1 + kCompileThreads / kWave);
+    const size_t lds = sizeof(int32_t) * (2 * (size_t)p.num_reqs + 1 + 5 * (kCompileThreads / kWave));
     hipLaunchKernelGGL(compile_kernel, dim3(p.num_token_tiles + 1), dim3(kCompileThreads), lds, s, p);
     return hipGetLastError();
 }
