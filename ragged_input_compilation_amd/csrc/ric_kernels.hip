@@ -23,19 +23,38 @@ namespace {
 
 constexpr int kWave = 64;
 
+// Scans across a 64-lane wave with DPP (data-parallel lane moves between
+// registers, no LDS traffic): row shifts by 1, 2, 4 and 8 scan each row of 16
+// lanes, then lane 15 is broadcast into rows 1 and 3 and lane 31 into rows 2
+// and 3, which carries the row totals across the wave.  A lane whose source
+// lies outside its row, or whose row the mask leaves out, keeps `identity`.
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_move(int identity, int x) {
+    return __builtin_amdgcn_update_dpp(identity, x, CTRL, ROW_MASK, 0xf, false);
+}
+
 __device__ __forceinline__ int wave_inclusive_scan(int x) {
-    const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int y = __shfl_up(x, d, kWave);
-        if (lane >= d) x += y;
-    }
+    x += dpp_move<kDppRowShr1, 0xf>(0, x);
+    x += dpp_move<kDppRowShr2, 0xf>(0, x);
+    x += dpp_move<kDppRowShr4, 0xf>(0, x);
+    x += dpp_move<kDppRowShr8, 0xf>(0, x);
+    x += dpp_move<kDppRowBcast15, 0xa>(0, x);
+    x += dpp_move<kDppRowBcast31, 0xc>(0, x);
     return x;
 }
 
-__device__ __forceinline__ int wave_max(int x) {
-#pragma unroll
-    for (int d = kWave / 2; d > 0; d >>= 1) x = max(x, __shfl_xor(x, d, kWave));
+// Running maximum over lanes 0..l; lane 63 holds the wave's maximum.
+__device__ __forceinline__ int wave_inclusive_max(int x) {
+    constexpr int lo = -2147483647 - 1;
+    x = max(x, dpp_move<kDppRowShr1, 0xf>(lo, x));
+    x = max(x, dpp_move<kDppRowShr2, 0xf>(lo, x));
+    x = max(x, dpp_move<kDppRowShr4, 0xf>(lo, x));
+    x = max(x, dpp_move<kDppRowShr8, 0xf>(lo, x));
+    x = max(x, dpp_move<kDppRowBcast15, 0xa>(lo, x));
+    x = max(x, dpp_move<kDppRowBcast31, 0xc>(lo, x));
     return x;
 }
 
@@ -71,8 +90,8 @@ __device__ __forceinline__ void block_scan2_max2(int a[2], int m[2], int* tmp, i
     const int wid = threadIdx.x / kWave;
     const int inc0 = wave_inclusive_scan(a[0]);
     const int inc1 = wave_inclusive_scan(a[1]);
-    const int m0 = wave_max(m[0]);
-    const int m1 = wave_max(m[1]);
+    const int m0 = wave_inclusive_max(m[0]);   // the wave's maximum at lane 63
+    const int m1 = wave_inclusive_max(m[1]);
     if (lane == kWave - 1) {
         tmp[4 * wid + 0] = inc0;
         tmp[4 * wid + 1] = inc1;

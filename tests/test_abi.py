@@ -176,7 +176,8 @@ def build_c_step(out_path, ric):
     libdir = os.path.dirname(ric.LIB_PATH)
     subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
                     "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", src, "-o", str(out_path),
-                    "-L", libdir, "-lric", "-L", "/opt/rocm/lib", "-lamdhip64", f"-Wl,-rpath,{libdir}"],
+                    "-L", libdir, "-l:" + os.path.basename(ric.LIB_PATH), "-L", "/opt/rocm/lib", "-lamdhip64",
+                    f"-Wl,-rpath,{libdir}"],
                    check=True, capture_output=True, text=True)
     return str(out_path)
 
