@@ -7,11 +7,13 @@
  * loops; shares nothing with the HIP code.
  *
  * Sources:
- *   [P5] "Nano-VLLM全代码解析笔记(4)-model_runner": prepare_prefill walks each
- *        sequence from its cached length to cached + scheduled, appends the
- *        token ids and positions, grows cu_seqlens_q / cu_seqlens_k, and emits
- *        K/V slots one physical block at a time as a contiguous range; its
- *        Q&A item 14 works the block-range loop by hand.
+ *   [P5] "Nano-VLLM全代码解析笔记(4)-model_runner": the prefill inputs cover
+ *        each sequence from its cached length to cached + scheduled, with
+ *        running totals of query and key lengths (cu_seqlens_q / _k), and the
+ *        K/V slots come one physical block at a time as contiguous ranges
+ *        (prepare_prefill; Q&A item 14 works such ranges by hand).  Written
+ *        here as the intersection of each request's position interval with
+ *        each block's interval.
  *   [P1] "vLLM 源码完全拆解（五）…" §第四步 (logits index = last token of each
  *        request) and §Chunked Prefill (partial prompts are discarded).
  *   [P3] "变长批处理与一次混合前向" §练习 1 (compacted logits list).
@@ -58,53 +60,49 @@ int nano_compile(const nano_in* in, nano_out* out)
 {
     const int32_t B = in->block_size;
     int32_t n = 0;                 /* tokens emitted so far */
-    int32_t n_slots = 0;           /* slots emitted so far  */
     int32_t max_q = 0, max_k = 0;
     int32_t i, k;
 
     out->query_start_loc[0] = 0;
     out->cu_seqlens_k[0] = 0;
     for (i = 0; i < in->num_reqs; ++i) {
-        const int32_t start = in->num_computed[i];
-        const int32_t seqlen_q = in->num_scheduled[i];
-        const int32_t end = start + seqlen_q;
-        const int32_t* tok = in->tokens + (int64_t)i * in->tok_stride;
-        const int32_t* table = in->blocks + (int64_t)i * in->blk_stride;
-        int32_t pos, blk, first_block, end_block;
+        const int32_t cached = in->num_computed[i];
+        const int32_t fresh = in->num_scheduled[i];
+        const int32_t total = cached + fresh;           /* key length after this step */
+        const int32_t* history = in->tokens + (int64_t)i * in->tok_stride;
+        const int32_t* owned = in->blocks + (int64_t)i * in->blk_stride;
+        int32_t b;
 
-        if (n + seqlen_q > in->n_pad)
+        if (fresh > in->n_pad - n)
             return -1;
-        for (pos = start; pos < end; ++pos) {
-            out->input_ids[n] = tok[pos];
-            out->positions[n] = pos;
-            out->req_indices[n] = i;
-            ++n;
-        }
-        out->query_start_loc[i + 1] = out->query_start_loc[i] + seqlen_q;
-        out->cu_seqlens_k[i + 1] = out->cu_seqlens_k[i] + end;
-        if (seqlen_q > max_q) max_q = seqlen_q;
-        if (end > max_k) max_k = end;
+        out->query_start_loc[i + 1] = out->query_start_loc[i] + fresh;
+        out->cu_seqlens_k[i + 1] = out->cu_seqlens_k[i] + total;
+        out->seq_lens[i] = total;
+        max_q = fresh > max_q ? fresh : max_q;
+        max_k = total > max_k ? total : max_k;
 
-        /* One contiguous slot range per touched physical block. */
-        first_block = start / B;
-        end_block = (end + B - 1) / B;
-        for (blk = first_block; blk < end_block; ++blk) {
-            int32_t slot_start = table[blk] * B;
-            int32_t slot_end;
-            int32_t s;
-            if (blk == first_block)
-                slot_start += start % B;
-            if (blk != end_block - 1)
-                slot_end = table[blk] * B + B;
-            else
-                slot_end = table[blk] * B + (end - blk * B);
-            for (s = slot_start; s < slot_end; ++s)
-                out->slot_mapping[n_slots++] = s;
+        /* The new tokens are positions [cached, total) of the history. */
+        for (k = 0; k < fresh; ++k) {
+            out->input_ids[n + k] = history[cached + k];
+            out->positions[n + k] = cached + k;
+            out->req_indices[n + k] = i;
         }
 
-        out->seq_lens[i] = end;
+        /* Their K/V slots, one physical block at a time: logical block b
+         * covers positions [b*B, (b+1)*B); the part of [cached, total) that
+         * falls inside it maps to consecutive slots of physical block
+         * owned[b], at the same offsets within the block. */
+        for (b = cached / B; b * B < total; ++b) {
+            const int32_t lo = cached > b * B ? cached : b * B;
+            const int32_t hi = total < (b + 1) * B ? total : (b + 1) * B;
+            int32_t p;
+            for (p = lo; p < hi; ++p)
+                out->slot_mapping[n + (p - cached)] = owned[b] * B + (p - b * B);
+        }
+        n += fresh;
+
         out->logits_indices[i] = out->query_start_loc[i + 1] - 1;
-        out->discard[i] = (uint8_t)(end < in->num_prompt[i] ? 1 : 0);
+        out->discard[i] = (uint8_t)(total < in->num_prompt[i] ? 1 : 0);
     }
     out->num_actual_tokens = n;
     out->max_seqlen_q = max_q;

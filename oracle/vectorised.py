@@ -4,9 +4,10 @@ Test infrastructure only.  This is the array formulation the pages describe for
 the CPU side of the runner, used here as a second, independently written
 oracle that the per-token loops in ``step`` must agree with:
 
-* request expansion by ``repeat`` and in-request offsets by ``arange`` minus
-  the repeated exclusive prefix sum ([P2 §8.3.1.6 np.repeat + cumsum 的向量化
-  req_indices 构造]);
+* request expansion by ``repeat`` of the request numbers by their scheduled
+  counts ([P1 §为什么删除后还要压紧], [P2 §8.3.1.6]); a token's index
+  inside its request is its flat index minus the start of its request,
+  gathered from the exclusive prefix sum;
 * the token gather as one ``take`` from the flattened [rows, max_model_len]
   table at ``row * max_model_len + position`` ([P2 §8.3.1.7 torch.index_select
   而不是 np.take]; [P1 §第三步：从二维 token 历史抽取本轮切片]);
@@ -34,9 +35,9 @@ def compile_arrays(c, q, P, token_table, block_table, *, block_size: int,
 
     cu = np.cumsum(q)
     N = int(cu[-1]) if R else 0
+    starts = cu - q                                    # first flat index of each request
     req_indices = np.repeat(np.arange(R), q)
-    offsets = np.repeat(cu - q, q)
-    query_pos = np.arange(N) - offsets
+    query_pos = np.arange(N) - starts[req_indices]
     positions = c[req_indices] + query_pos
     input_ids = np.take(token_table.reshape(-1), req_indices * M + positions)
     block_numbers = np.take(block_table.reshape(-1), req_indices * nblk + positions // block_size)

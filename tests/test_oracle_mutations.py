@@ -109,7 +109,7 @@ PY_MUTANTS = [
 ]
 
 NP_MUTANTS = [
-    ("offsets = np.repeat(cu - q, q)", "offsets = np.repeat(cu, q)"),
+    ("starts = cu - q ", "starts = cu "),
     ("positions // block_size)", "positions % block_size)"),
     ("req_indices * M + positions", "req_indices + positions * M"),
     ("logits[:R] = qsl[1:R + 1] - 1", "logits[:R] = qsl[:R]"),
@@ -117,12 +117,14 @@ NP_MUTANTS = [
 ]
 
 C_MUTANTS = [
-    ("slot_start += start % B;", ";"),
-    ("end_block = (end + B - 1) / B;", "end_block = end / B;"),
-    ("slot_end = table[blk] * B + (end - blk * B);", "slot_end = table[blk] * B + B;"),
+    ("const int32_t lo = cached > b * B ? cached : b * B;", "const int32_t lo = b * B;"),        # offset in the first block dropped
+    ("for (b = cached / B; b * B < total; ++b) {", "for (b = cached / B; (b + 1) * B <= total; ++b) {"),  # partial last block dropped
+    ("const int32_t hi = total < (b + 1) * B ? total : (b + 1) * B;", "const int32_t hi = (b + 1) * B;"),  # whole last block
+    ("out->slot_mapping[n + (p - cached)] = owned[b] * B + (p - b * B);",
+     "out->slot_mapping[n + (p - cached)] = owned[b] * B + (p - cached);"),                          # offset from the wrong origin
     ("out->logits_indices[i] = out->query_start_loc[i + 1] - 1;",
      "out->logits_indices[i] = out->query_start_loc[i];"),
-    ("out->positions[n] = pos;", "out->positions[n] = pos - start;"),
+    ("out->positions[n + k] = cached + k;", "out->positions[n + k] = k;"),
 ]
 
 
