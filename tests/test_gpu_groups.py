@@ -1,6 +1,7 @@
 """GPU parity for several KV-cache groups: per-group block tables and slot
 mappings, a group without per-token slots, manager-to-kernel block expansion
-of the exported table, and condense moving every group's row."""
+of the exported table, condense moving every group's row, and every
+group's slots following counts corrected on the device."""
 import numpy as np
 import pytest
 import torch
@@ -112,4 +113,58 @@ def test_groups_compile_tables_and_condense(rt):
         ric.ric_append_blocks_group(b.h, rid0, 3, [1])          # no such group
     with pytest.raises(ric.RicError):
         ric.ric_append_blocks_group(b.h, rid0, 2, [POOL2])      # outside group 2's pool
+    b.close()
+
+
+def test_group_slots_follow_corrected_counts(rt):
+    """Counts corrected on the device (asynchronous speculative decoding) move
+    every group's slots with them: group 0's compile and group 1's slot
+    mapping equal the oracle's on the corrected positions."""
+    ric, runner = rt
+    rng = np.random.default_rng(62)
+    MR, R = 16, 12
+    b = runner.Batch(_cfg(ric, MR, 64))
+    ref = ref_batch.RefBatch(MR, M, M // B0, POOL0)
+    p0 = list(rng.permutation(np.arange(1, POOL0)))
+    p1 = list(rng.permutation(np.arange(1, POOL1)))
+    c_opt, d = [], []
+    for rid in range(R):
+        T = int(rng.integers(8, 400))
+        toks = rng.integers(0, 50000, T)
+        b0 = [int(p0.pop()) for _ in range(-(-T // B0))]
+        b1 = [int(p1.pop()) for _ in range(-(-T // B1))]
+        ric.ric_add_request(b.h, rid, toks, T, T - 1, b0)
+        ref.add_request(rid, toks, T, T - 1, b0)
+        ric.ric_append_blocks_group(b.h, rid, 1, b1)
+        ref.append_blocks_group(rid, 1, b1)
+        d.append(int(rng.integers(0, 4)))
+        c_opt.append(T - 1)
+    ric.ric_schedule(b.h, c_opt, [1] * R)
+    ref.schedule(c_opt, [1] * R)
+    pos_of = [int(x) for x in rng.permutation(R)]
+    acc = np.zeros(R, np.int32)
+    kept = np.full((R, 4), -1, np.int32)
+    for i in range(R):
+        v = int(rng.integers(1, d[i] + 2))
+        acc[pos_of[i]] = v
+        kept[pos_of[i], :v] = rng.integers(90000, 99999, v)
+    acc_dev, kept_dev = torch.from_numpy(acc).cuda(), torch.from_numpy(kept).cuda()
+    rows = list(range(R))
+    ric.ric_correct_computed(b.h, rows, pos_of, d, acc_dev.data_ptr(), R, kept_dev.data_ptr(), 4)
+    cc = [ref.rows[i].num_computed for i in range(R)]
+    assert ref_step.correct_computed(cc, [ref.rows[i].tokens for i in range(R)], rows, pos_of, d, acc,
+                                     kept.tolist()) == 0
+    for i in range(R):
+        ref.rows[i].num_computed = cc[i]
+    want = ref_step.compile_step(ref.step_rows(), block_size=B0, max_num_reqs=MR, max_model_len=M,
+                                 max_num_batched_tokens=64, num_kv_blocks=POOL0, n_pad=R)
+    s = b.compile(R)
+    got = b.step_outputs(s)
+    for k in ("input_ids", "positions", "slot_mapping", "seq_lens", "cu_seqlens_k"):
+        assert np.array_equal(np.asarray(got[k], np.int64), np.asarray(want[k], np.int64)), k
+    want1 = ref_step.group_slot_mapping(want["positions"], want["req_indices"],
+                                        [ref.rows[i].group_blocks[1] for i in range(R)], B1)
+    got1 = ric.ric_read_device(s.group_slot_mapping[1], 4 * R, np.int32)
+    assert np.array_equal(got1.astype(np.int64), np.asarray(want1, np.int64))
+    assert any(cc[i] != c_opt[i] for i in range(R))          # some counts really moved
     b.close()
