@@ -93,13 +93,19 @@ def code_digest(text):
     return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()
 
 
-def kernel_source_digest():
+def kernel_source_digest(text=None):
     """Digest of the K/V write's code: its load/store helpers, both kernels and
     their launcher (the source from the load helper up to the row-gather
-    kernel), so that changes elsewhere in the file keep its counters valid."""
-    with open(os.path.join(ROOT, "ragged_input_compilation_amd", "csrc", "ric_kernels.hip"), encoding="utf-8") as f:
-        text = f.read()
-    return code_digest(text[text.index("u32x4 load16("):text.index("gather_kernel(")])
+    kernel), so that changes elsewhere in the file keep its counters valid.
+    ``text``: the kernel source (default: the file in the package)."""
+    if text is None:
+        with open(os.path.join(ROOT, "ragged_input_compilation_amd", "csrc", "ric_kernels.hip"),
+                  encoding="utf-8") as f:
+            text = f.read()
+    start, end = text.find("u32x4 load16("), text.find("gather_kernel(")
+    if start < 0 or end <= start:
+        raise ValueError("the K/V write's code is not where the digest expects it")
+    return code_digest(text[start:end])
 
 
 def load_traffic(kernel_name, workload_name):

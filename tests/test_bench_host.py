@@ -36,6 +36,23 @@ def test_code_digest_ignores_comments_only():
     assert bench.code_digest(code) != bench.code_digest(other)
 
 
+def test_kernel_digest_covers_the_kv_code_only():
+    """Edits to other kernels keep the K/V counters valid; an edit to the K/V
+    write's code voids them; a source without the K/V region is an error."""
+    with open(os.path.join(os.path.dirname(bench.__file__), "ragged_input_compilation_amd", "csrc",
+                           "ric_kernels.hip"), encoding="utf-8") as f:
+        text = f.read()
+    base = bench.kernel_source_digest(text)
+    assert base == bench.kernel_source_digest()
+    other = text.replace("__global__ __launch_bounds__(kCompileThreads) void compile_kernel(CompileParams p) {",
+                         "__global__ __launch_bounds__(kCompileThreads) void compile_kernel(CompileParams p) { int z = 0;")
+    assert other != text and bench.kernel_source_digest(other) == base
+    kv = text.replace("const int C = p.row_bytes >> 4;", "const int C = (p.row_bytes >> 4) + 0;", 1)
+    assert kv != text and bench.kernel_source_digest(kv) != base
+    with pytest.raises(ValueError):
+        bench.kernel_source_digest(text.replace("u32x4 load16(", "u32x4 load_16("))
+
+
 def test_load_traffic_needs_matching_code(tmp_path, monkeypatch):
     prof = tmp_path / "profiles"
     prof.mkdir()
