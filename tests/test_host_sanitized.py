@@ -8,7 +8,8 @@ groups), condense,
 sampled-token appends, schedules, corrections of optimistic computed counts
 and compiles, with a staging log small
 enough to force split uploads.  After every flush the column store equals the
-reference batch.  Any out-of-bounds access or undefined behaviour aborts."""
+reference batch.  The stateless K/V-write and gather calls then run their
+argument checks.  Any out-of-bounds access or undefined behaviour aborts."""
 import os
 import subprocess
 import sys
@@ -186,6 +187,41 @@ for step in range(600):
             check()
 check()
 ric.ric_destroy(h)
+
+# The stateless entry points' argument checks (the fake device runs no kernels).
+def rejects(fn, *a, **kw):
+    try:
+        fn(*a, **kw)
+    except ric.RicError as e:
+        return e.code
+    raise AssertionError("accepted")
+
+buf = np.zeros(1 << 16, np.uint8)
+base = (buf.ctypes.data + 255) // 256 * 256
+slots = np.zeros(8, np.int32)
+idx = np.zeros(8, np.int32)
+P = [base] * 40
+kv = ric.ric_reshape_and_cache
+kv(P, P, P, P, slots.ctypes.data, 8, 64, 100)                        # 40 layers: two launches
+kv(P[:3], P[:3], P[:3], P[:3], slots.ctypes.data, 8, 64, 100, src_row_stride=128)
+kv(P[:3], P[:3], P[:3], P[:3], slots.ctypes.data, 0, 64, 100)         # nothing to write
+for args, kw in (((P, P, P, P, slots.ctypes.data, 8, 24, 100), {{}}),                   # row not 16-byte multiple
+                 ((P, P, P, P, slots.ctypes.data, 8, 64, 100), dict(src_row_stride=32)),  # stride below the row
+                 ((P, P, P, [base + 8] * 40, slots.ctypes.data, 8, 64, 100), {{}}),        # misaligned cache
+                 ((P, P, P, P, slots.ctypes.data, (1 << 24) + 1, 64, 100), {{}}),         # above the launch limit
+                 ((P, P, P, P, slots.ctypes.data, 8, 64, 0), {{}}),                       # no slots
+                 ((P, P, P, P, slots.ctypes.data, 8, 64, 100), dict(flags=1)),          # unknown flag
+                 ((P, P, P, P, 0, 8, 64, 100), {{}})):                                   # no slot mapping
+    assert rejects(kv, *args, **kw) == ric.RIC_EINVAL, (args[5:], kw)
+g = ric.ric_gather_rows
+g(base, 64, 8, idx.ctypes.data, 0, 8, 64, base + 4096)
+g(base, 64, 8, idx.ctypes.data, 0, 0, 64, base + 4096)                # no rows
+for args in ((base, 64, 8, idx.ctypes.data, 0, 8, 40, base + 4096),     # row not 16-byte multiple
+             (base, 32, 8, idx.ctypes.data, 0, 8, 64, base + 4096),     # source stride below the row
+             (base + 8, 64, 8, idx.ctypes.data, 0, 8, 64, base + 4096), # misaligned source
+             (base, 64, -1, idx.ctypes.data, 0, 8, 64, base + 4096),    # negative source rows
+             (base, 64, 8, idx.ctypes.data, 0, (1 << 24) + 1, 64, base + 4096)):
+    assert rejects(g, *args) == ric.RIC_EINVAL, args
 print("sanitized control plane ok", next_id, "corrections", corrections)
 """
 
