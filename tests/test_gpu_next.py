@@ -168,9 +168,9 @@ def test_async_spec_decode_correction_loop(rt):
     asynchronous one: the host schedules every row as if all its drafts had
     been accepted, and ric_correct_computed lowers the counts on the device
     from an accepted-count array in the sampler's own order, writing the last
-    kept token into the history.  Afterwards the host learns what was kept,
-    drops the rejected drafts (ric_truncate_tokens) and appends the step's new
-    token.  Two requests finish and the batch is condensed midway.  Every
+    kept token into the history.  Afterwards the host learns what was kept and
+    drops the rejected drafts (ric_truncate_tokens), and the step's new token
+    is appended from the device (ric_append_sampled).  Two requests finish and the batch is condensed midway.  Every
     compile, the device's computed counts and histories equal the oracle's."""
     ric, runner = rt
     rng = np.random.default_rng(33)
@@ -266,15 +266,19 @@ def test_async_spec_decode_correction_loop(rt):
             assert cc[i] == c[i] + v[i]
         compile_and_compare((rnd, "async"))
         # the host learns what was kept: rejected drafts leave the history,
-        # and the async step's own sampled token follows the kept ones
+        # and the async step's own sampled token (still on the device, in the
+        # sampler's order) follows the kept ones
         for i, rid in enumerate(order):
             keep = c[i] + v[i] + 1
             ric.ric_truncate_tokens(b.h, rid, keep)
             ref.truncate_tokens(rid, keep)
-            y = int(rng.integers(0, 50000))
-            ric.ric_append_tokens(b.h, rid, [y])
-            ref.append_tokens(rid, [y])
             count[rid] = keep
+        y = rng.integers(0, 50000, R).astype(np.int32)
+        y_dev = torch.from_numpy(y).cuda()
+        y_pos = [int(x) for x in rng.permutation(R)]          # row i's token at y[y_pos[i]]
+        ric.ric_append_sampled(b.h, list(range(R)), y_dev.data_ptr(), R, y_pos)
+        for i, rid in enumerate(order):
+            ref.append_tokens(rid, [int(y[y_pos[i]])])
     assert int(status.item()) == 0
 
     # out-of-range kept counts leave their rows alone and are counted
