@@ -28,6 +28,8 @@ constexpr int kWave = 64;
 // lanes, then lane 15 is broadcast into rows 1 and 3 and lane 31 into rows 2
 // and 3, which carries the row totals across the wave.  A lane whose source
 // lies outside its row, or whose row the mask leaves out, keeps `identity`.
+// All 64 lanes must be active: callers reach these with every thread of a
+// full-wave workgroup.
 constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
 constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
 
