@@ -232,7 +232,11 @@ int ric_replace_blocks_group(ric_batch* b, uint64_t req_id, int32_t group, const
  * deltas first. */
 int ric_condense(ric_batch* b, int32_t* out_num_moved);
 
-/* Upload staged deltas now. */
+/* Upload staged deltas now.  Uploads are refused with ESTATE (nothing
+ * changes) while the handle's stream is being captured into a graph: every
+ * call that flushes (this one, ric_condense, ric_compile, ric_append_sampled,
+ * ric_spec_decode_metadata, ric_correct_computed, ric_block_table_padded)
+ * must find the log empty during a capture, so flush before capturing. */
 int ric_flush(ric_batch* b);
 
 /* Append one token per listed row from a DEVICE array: last step's sampled ids
@@ -358,7 +362,10 @@ int ric_schedule(ric_batch* b, int32_t num_reqs, const int32_t* num_computed,
  * ([P1 §第一步..第四步], [P1 §Block table 是逐请求的页表], [P3 §布局与元数据]).
  * Tokens [N, num_tokens_padded) are padding: they map to the null block
  * ([P1 §固定地址与动态有效长度如何共存], [P4 §5]).  Requires a ric_schedule
- * since the last row-changing call.  Errors: ESTATE, EINVAL (N > N_pad or
+ * since the last row-changing call.  A compile captured into a graph replays
+ * the R and num_tokens_padded it was captured with (the counts themselves are
+ * read from the device columns at replay), and needs an empty delta log at
+ * capture (see ric_flush).  Errors: ESTATE, EINVAL (N > N_pad or
  * N_pad > max_num_batched_tokens). */
 int ric_compile(ric_batch* b, int32_t num_tokens_padded, ric_step* out);
 
@@ -395,6 +402,27 @@ int ric_reshape_and_cache(const void* const* k, const void* const* v, void* cons
 int ric_gather_rows(const void* src, int64_t src_row_stride, int64_t src_rows,
                     const int32_t* idx, const int32_t* dev_count, int32_t max_rows,
                     int32_t row_bytes, void* dst, int64_t dst_row_stride, int32_t* dev_status,
+                    void* stream);
+
+/* Slot-collision check of a step's slot mapping (a debugging aid, not a step
+ * call).  Every real token must own its cache slot: two tokens writing one
+ * slot would leave a K/V row that depends on the order of the writes (each
+ * block has a single owner, [P1 §八条必须成立的不变量], item 7).  For the first n slots, n =
+ * num_tokens, or min(num_tokens, *dev_num_tokens) when dev_num_tokens (a
+ * DEVICE int32, e.g. ric_step.dev_scalars + 1 for N) is given:
+ *   dev_result[0] += tokens whose slot an earlier-checked token of the same
+ *                    call also holds (k tokens on one slot add k - 1)
+ *   dev_result[1] += slots outside [0, num_slots)
+ * dev_result is a DEVICE int32[2] the caller zeroes.  Pass the real token
+ * count N, not the padded one: padded tokens all share the null block.
+ *   workspace  DEVICE buffer of at least ric_check_slots_workspace_bytes(
+ *              num_slots) bytes (a bitmap of one bit per slot), 4-byte
+ *              aligned, owned by the caller, cleared by the call itself
+ * Two launches on `stream`; nothing is read back.  Errors: EINVAL (counts,
+ * NULL or misaligned pointers, workspace too small), EHIP. */
+size_t ric_check_slots_workspace_bytes(int64_t num_slots);   /* 0 if num_slots outside [1, 2^31] */
+int ric_check_slots(const int32_t* slot_mapping, int32_t num_tokens, const int32_t* dev_num_tokens,
+                    int64_t num_slots, void* workspace, size_t workspace_bytes, int32_t* dev_result,
                     void* stream);
 
 /* ---- host-only helpers (no device work) ----------------------------------- */

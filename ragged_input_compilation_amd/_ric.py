@@ -115,6 +115,9 @@ def _load():
             ctypes.c_uint32, _vp]),
         "ric_gather_rows": (ctypes.c_int, [_vp, ctypes.c_int64, ctypes.c_int64, _vp, _vp, ctypes.c_int32,
                                            ctypes.c_int32, _vp, ctypes.c_int64, _vp, _vp]),
+        "ric_check_slots_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64]),
+        "ric_check_slots": (ctypes.c_int, [_vp, ctypes.c_int32, _vp, ctypes.c_int64, _vp, ctypes.c_size_t, _vp,
+                                           _vp]),
         "ric_padded_size": (ctypes.c_int32, [_i32p, ctypes.c_int32, ctypes.c_int32]),
         "ric_condense_plan": (ctypes.c_int32, [_u8p, ctypes.c_int32, _i32p, _i32p]),
         "ric_check_step": (ctypes.c_int, [ctypes.POINTER(ric_config), ctypes.c_int32] + [_i32p] * 5 +
@@ -349,6 +352,17 @@ def ric_gather_rows(src: int, src_row_stride: int, src_rows: int, idx: int, dev_
                     stream: int = 0) -> None:
     _err(_lib.ric_gather_rows(_vp(src), src_row_stride, src_rows, _vp(idx), _vp(dev_count or None), max_rows,
                               row_bytes, _vp(dst), dst_row_stride, _vp(dev_status or None),
+                              _vp(stream or None)))
+
+
+def ric_check_slots_workspace_bytes(num_slots: int) -> int:
+    return int(_lib.ric_check_slots_workspace_bytes(num_slots))
+
+
+def ric_check_slots(slot_mapping: int, num_tokens: int, num_slots: int, workspace: int, workspace_bytes: int,
+                    dev_result: int, dev_num_tokens: int = 0, stream: int = 0) -> None:
+    _err(_lib.ric_check_slots(_vp(slot_mapping or None), num_tokens, _vp(dev_num_tokens or None), num_slots,
+                              _vp(workspace or None), workspace_bytes, _vp(dev_result or None),
                               _vp(stream or None)))
 
 

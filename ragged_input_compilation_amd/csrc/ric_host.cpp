@@ -318,11 +318,27 @@ int stage(ric_batch* b, void* dst, const void* src, size_t n) {
     return RIC_OK;
 }
 
+// A graph captured during an upload would record the copy from a pinned log
+// that later flushes rewrite, and an apply kernel whose op count and offsets
+// belong to that one flush: a replay would scatter whatever the log then
+// holds.  Uploads therefore happen outside capture only; calls that stage and
+// upload in one go check this before they stage anything.
+int refuse_if_capturing(ric_batch* b) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    HIP_TRY(hipStreamIsCapturing(b->stream, &cap));
+    if (cap != hipStreamCaptureStatusNone)
+        return fail(RIC_ESTATE, "staged deltas cannot be uploaded while the handle's stream is being captured: "
+                                "flush (ric_flush, or an eager step) before the capture begins");
+    return RIC_OK;
+}
+
 int flush(ric_batch* b) {
     bool any_dirty = false;
     for (int c = 0; c < kNumScalarCols; ++c) any_dirty |= b->dirty_lo[c] < b->dirty_hi[c];
     if (b->ops.empty() && !any_dirty) return RIC_OK;
-    int rc = ensure_log_writable(b);
+    int rc = refuse_if_capturing(b);
+    if (rc) return rc;
+    rc = ensure_log_writable(b);
     if (rc) return rc;
     // Scalar columns: copy the dirty row range of each column from the mirror.
     // (Room for them is always reserved by log_need.)
@@ -702,6 +718,8 @@ int ric_condense(ric_batch* b, int32_t* out_num_moved) {
     std::vector<int32_t> holes(MR), srcs(MR);
     const int32_t np = ric_condense_plan(b->live.data(), MR, holes.data(), srcs.data());
     if (np > 0) {
+        int rc = refuse_if_capturing(b);
+        if (rc) return rc;
         // The pair list rides in the log with any staged deltas; the flush
         // applies them all before the move kernel runs on the same stream.
         std::vector<int32_t> pairs(2 * (size_t)np);
@@ -711,7 +729,7 @@ int ric_condense(ric_batch* b, int32_t* out_num_moved) {
             pairs[2 * k + 1] = srcs[k];
             max_T = std::max(max_T, b->S(kNumTokens, srcs[k]));
         }
-        int rc = stage(b, b->d_pairs, pairs.data(), pairs.size());
+        rc = stage(b, b->d_pairs, pairs.data(), pairs.size());
         if (rc) return rc;
         rc = flush(b);
         if (rc) return rc;
@@ -766,7 +784,9 @@ int ric_append_sampled(ric_batch* b, int32_t n, const int32_t* rows, const int32
             return fail(RIC_EINVAL, "source index %d outside [0, %d)", idx[k], dev_tokens_len);
         off[k] = (int64_t)r * b->L.tok_stride + T;
     }
-    int rc = stage(b, b->d_samp_off, off.data(), 2 * (size_t)n);
+    int rc = refuse_if_capturing(b);
+    if (rc) return rc;
+    rc = stage(b, b->d_samp_off, off.data(), 2 * (size_t)n);
     if (rc) return rc;
     rc = stage(b, b->d_samp_idx, idx.data(), (size_t)n);
     if (rc) return rc;
@@ -797,7 +817,9 @@ int ric_spec_decode_metadata(ric_batch* b, const int32_t* num_draft_tokens, ric_
         num_logits += d + 1;
         num_draft += d;
     }
-    int rc = stage(b, b->d_spec_d, num_draft_tokens, (size_t)R);
+    int rc = refuse_if_capturing(b);
+    if (rc) return rc;
+    rc = stage(b, b->d_spec_d, num_draft_tokens, (size_t)R);
     if (rc) return rc;
     rc = flush(b);
     if (rc) return rc;
@@ -855,7 +877,9 @@ int ric_correct_computed(ric_batch* b, int32_t n, const int32_t* rows, const int
                         d + 1, r);
     }
     const int MR = b->cfg.max_num_reqs;
-    int rc = stage(b, b->d_corr, rows, (size_t)n);
+    int rc = refuse_if_capturing(b);
+    if (rc) return rc;
+    rc = stage(b, b->d_corr, rows, (size_t)n);
     if (rc) return rc;
     rc = stage(b, b->d_corr + MR, prev_index, (size_t)n);
     if (rc) return rc;
@@ -1175,6 +1199,30 @@ int ric_gather_rows(const void* src, int64_t src_row_stride, int64_t src_rows, c
     p.max_rows = max_rows;
     p.row_bytes = row_bytes;
     HIP_TRY(launch_gather(p, static_cast<hipStream_t>(stream)));
+    return RIC_OK;
+}
+
+size_t ric_check_slots_workspace_bytes(int64_t num_slots) {
+    if (num_slots <= 0 || num_slots > (int64_t(1) << 31)) return 0;
+    return align_up((size_t)((num_slots + 31) / 32) * 4, kAlign);
+}
+
+int ric_check_slots(const int32_t* slot_mapping, int32_t num_tokens, const int32_t* dev_num_tokens,
+                    int64_t num_slots, void* workspace, size_t workspace_bytes, int32_t* dev_result,
+                    void* stream) {
+    if (num_tokens < 0 || num_tokens > kMaxRowsPerLaunch)
+        return fail(RIC_EINVAL, "num_tokens %d outside [0, %d]", num_tokens, kMaxRowsPerLaunch);
+    if (num_slots <= 0 || num_slots > (int64_t(1) << 31))
+        return fail(RIC_EINVAL, "num_slots %lld outside [1, 2^31]", (long long)num_slots);
+    if (!dev_result || (num_tokens > 0 && !slot_mapping)) return fail(RIC_EINVAL, "NULL pointer argument");
+    if (!workspace || reinterpret_cast<uintptr_t>(workspace) % 4 != 0)
+        return fail(RIC_EINVAL, "workspace is NULL or not 4-byte aligned");
+    const size_t need = (size_t)((num_slots + 31) / 32) * 4;
+    if (workspace_bytes < need)
+        return fail(RIC_EINVAL, "workspace of %zu bytes, %zu needed for %lld slots", workspace_bytes, need,
+                    (long long)num_slots);
+    HIP_TRY(launch_check_slots(slot_mapping, num_tokens, dev_num_tokens, num_slots,
+                               static_cast<uint32_t*>(workspace), dev_result, static_cast<hipStream_t>(stream)));
     return RIC_OK;
 }
 

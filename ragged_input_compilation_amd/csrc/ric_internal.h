@@ -165,6 +165,12 @@ hipError_t launch_correct_computed(const CorrectParams& p, hipStream_t s);
 hipError_t launch_append_sampled(int32_t* tokens, const int64_t* dst_off, const int32_t* src_idx,
                                  const int32_t* src, int32_t src_len, int32_t n, int32_t* err, hipStream_t s);
 
+// Clears ceil(num_slots / 32) bitmap words, then counts, for the first
+// min(n, *dev_n) slots (n when dev_n is null), collisions in result[0] and
+// slots outside [0, num_slots) in result[1].
+hipError_t launch_check_slots(const int32_t* slot, int32_t n, const int32_t* dev_n, int64_t num_slots,
+                              uint32_t* bits, int32_t* result, hipStream_t s);
+
 // Token tile of one compile workgroup.
 constexpr int kCompileThreads = 256;
 constexpr int kCompileTokensPerThread = 1;

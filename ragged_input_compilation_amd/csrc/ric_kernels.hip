@@ -13,6 +13,8 @@
 // gather are indexed copies bound by HBM bandwidth.  The copies move 16-byte
 // vectors per lane, use non-temporal accesses where a byte is touched once per
 // step and the measurements favour them, and compute byte offsets in 64 bits.
+#include <algorithm>
+
 #include "ric_internal.h"
 
 namespace ric {
@@ -686,6 +688,44 @@ __global__ __launch_bounds__(256) void correct_computed_kernel(CorrectParams p) 
 hipError_t launch_correct_computed(const CorrectParams& p, hipStream_t s) {
     if (p.n == 0) return hipSuccess;
     hipLaunchKernelGGL(correct_computed_kernel, dim3((p.n + 255) / 256), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Slot-collision check: every real token must own its cache slot, since two
+// tokens writing one slot leave a result that depends on the order of the
+// writes (each block has a single owner, [P1 §八条必须成立的不变量], item 7).  A bitmap of
+// ceil(num_slots / 32) words is cleared, then each token sets its slot's bit;
+// a token that finds the bit already set counts one collision.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void clear_words_kernel(uint32_t* words, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) words[i] = 0u;
+}
+
+__global__ __launch_bounds__(256) void mark_slots_kernel(const int32_t* slot, int32_t n, const int32_t* dev_n,
+                                                         int64_t num_slots, uint32_t* bits, int32_t* result) {
+    int count = n;
+    if (dev_n != nullptr) count = min(count, max(0, *dev_n));
+    for (int t = blockIdx.x * 256 + threadIdx.x; t < count; t += gridDim.x * 256) {
+        const int s = slot[t];
+        if (s < 0 || (int64_t)s >= num_slots) {
+            atomicAdd(result + 1, 1);
+            continue;
+        }
+        const uint32_t m = 1u << (s & 31);
+        if (atomicOr(bits + (s >> 5), m) & m) atomicAdd(result, 1);
+    }
+}
+
+hipError_t launch_check_slots(const int32_t* slot, int32_t n, const int32_t* dev_n, int64_t num_slots,
+                              uint32_t* bits, int32_t* result, hipStream_t s) {
+    const int64_t words = (num_slots + 31) / 32;
+    const int gc = (int)std::min<int64_t>((words + 255) / 256, 4096);
+    hipLaunchKernelGGL(clear_words_kernel, dim3(gc), dim3(256), 0, s, bits, words);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || n == 0) return e;
+    const int gm = std::min((n + 255) / 256, 4096);
+    hipLaunchKernelGGL(mark_slots_kernel, dim3(gm), dim3(256), 0, s, slot, n, dev_n, num_slots, bits, result);
     return hipGetLastError();
 }
 

@@ -65,6 +65,52 @@ def u16(t: torch.Tensor) -> torch.Tensor:
     return t.view(torch.int16)
 
 
+def check_cache_exact(cache: torch.Tensor, src: torch.Tensor, slots: np.ndarray, num_real: int,
+                      sentinel16: int, num_slots: int, null_rows=(0, 0), label: str = "",
+                      chunk_rows: int = 1 << 18) -> None:
+    """Whole-cache byte check of one K or V cache after a write, on the device.
+
+    ``slots``: the oracle's slot list (int, at least num_real entries); token t
+    of ``src`` (rows of the same byte size as a cache row) belongs at slot[t].
+    Checks (1) every real row: cache[slot[t]] == src[t] for all t < num_real;
+    (2) every other row outside ``null_rows`` = [lo, hi) still holds the
+    sentinel in every byte: the set of rows holding any non-sentinel word,
+    null rows excluded, must equal the set of real slots.  The null block is
+    excluded because padded tokens write there."""
+    row_bytes = cache.numel() * cache.element_size() // num_slots
+    assert row_bytes % 8 == 0
+    flat16 = cache.view(torch.int16).reshape(num_slots, row_bytes // 2)
+    src16 = src.reshape(src.shape[0], -1).view(torch.int16)
+    assert src16.shape[1] == row_bytes // 2
+    s_all = torch.from_numpy(np.asarray(slots[:num_real], np.int64)).to(cache.device)
+    for a in range(0, num_real, 8192):
+        b = min(num_real, a + 8192)
+        got = flat16[s_all[a:b]]
+        want = src16[a:b]
+        if not torch.equal(got, want):
+            bad = (got != want).any(dim=1).nonzero().flatten()
+            t = a + int(bad[0])
+            raise AssertionError(f"{label}: {bad.numel()} real rows differ in tokens [{a},{b}); first token {t} "
+                                 f"at slot {int(s_all[t])}")
+    pat = np.array([sentinel16 & 0xFFFF] * 4, np.uint16).view(np.int64)[0]
+    flat64 = cache.view(torch.int64).reshape(num_slots, row_bytes // 8)
+    found = []
+    for a in range(0, num_slots, chunk_rows):
+        b = min(num_slots, a + chunk_rows)
+        found.append((flat64[a:b] != int(pat)).any(dim=1).nonzero().flatten() + a)
+    found = torch.cat(found)
+    lo, hi = null_rows
+    found = found[(found < lo) | (found >= hi)]
+    expected = torch.unique(s_all)
+    expected = expected[(expected < lo) | (expected >= hi)]
+    if not torch.equal(found, expected):
+        extra = found[~torch.isin(found, expected)]
+        missing = expected[~torch.isin(expected, found)]
+        raise AssertionError(f"{label}: {extra.numel()} rows outside the step were written (first "
+                             f"{extra[:4].tolist()}), {missing.numel()} real slots still hold the sentinel "
+                             f"(first {missing[:4].tolist()})")
+
+
 def read_rows_i32(ptr_base_tensor, ptr, stride, rows, n) -> np.ndarray:
     """Rows [rows] of an int32 device matrix (at ptr, row stride in elements),
     first n columns, as numpy."""

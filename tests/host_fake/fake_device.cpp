@@ -73,6 +73,13 @@ hipError_t hipSetDevice(int device) {
     return hipSuccess;
 }
 const char* hipGetErrorString(hipError_t) { return "fake device"; }
+// Stream capture is simulated: the test switches it on and off.
+int g_capturing = 0;
+void fake_set_capturing(int on) { g_capturing = on; }
+hipError_t hipStreamIsCapturing(hipStream_t, hipStreamCaptureStatus* status) {
+    *status = g_capturing ? hipStreamCaptureStatusActive : hipStreamCaptureStatusNone;
+    return hipSuccess;
+}
 }
 
 namespace ric {
@@ -134,6 +141,23 @@ hipError_t launch_correct_computed(const CorrectParams& p, hipStream_t) {
         }
         p.computed[row] = c;
         if (p.sampled) p.tokens[(int64_t)row * p.tok_stride + c] = p.sampled[(int64_t)pos * p.sampled_stride + v - 1];
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_check_slots(const int32_t* slot, int32_t n, const int32_t* dev_n, int64_t num_slots,
+                              uint32_t* bits, int32_t* result, hipStream_t) {
+    std::memset(bits, 0, (size_t)((num_slots + 31) / 32) * 4);
+    const int count = dev_n ? std::min(n, std::max(0, *dev_n)) : n;
+    for (int t = 0; t < count; ++t) {
+        const int s = slot[t];
+        if (s < 0 || s >= num_slots) {
+            ++result[1];
+            continue;
+        }
+        const uint32_t m = 1u << (s & 31);
+        if (bits[s >> 5] & m) ++result[0];
+        bits[s >> 5] |= m;
     }
     return hipSuccess;
 }

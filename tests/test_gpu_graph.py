@@ -80,3 +80,36 @@ def test_captured_step_replays_match_eager(rt, name):
         assert torch.equal(out.view(torch.int16), hidden[logits].view(torch.int16)), f"{name} replay {rep}: gather"
     del g
     b.close()
+
+
+def test_capture_with_staged_deltas_is_refused(rt):
+    """A compile whose schedule is still staged must not be captured: the
+    upload would replay from a pinned log that later flushes rewrite.  The
+    call inside the capture fails with ESTATE and changes nothing; after the
+    capture the same compile runs eagerly and equals the oracle."""
+    ric, runner = rt
+    w = workloads.get("worked_example")
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        st = runner.current_stream()
+        b = runner.Batch(runner.config_of(w), stream=st)
+        b.load_history(w)
+        ref, order = replay_history(w)
+        b.schedule_from(w, order)            # the counts are staged, not yet uploaded
+        exp = expected_step(w, ref, use_python=True)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        codes = []
+        with torch.cuda.graph(g, stream=side):
+            for fn, a in ((ric.ric_compile, (b.h, exp["n_pad"])), (ric.ric_flush, (b.h,))):
+                try:
+                    fn(*a)
+                    codes.append(0)
+                except ric.RicError as e:
+                    codes.append(e.code)
+        assert codes == [ric.RIC_ESTATE, ric.RIC_ESTATE]
+        s = b.compile(exp["n_pad"])
+        torch.cuda.synchronize()
+        assert_step_equal(b.step_outputs(s), exp, "after a refused capture")
+    del g
+    b.close()

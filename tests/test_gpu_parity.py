@@ -1,17 +1,18 @@
 """GPU parity: libric on an MI355X against the CPU oracle, element by element.
 
 Compile outputs and the column store must be bit-exact; K/V cache rows and
-gathered hidden rows byte-exact.  Small cases are compared in full (every
-cache byte outside the null block); the full-size configurations compare the
-whole compile output and sampled cache rows, plus sentinel checks that nothing
-outside the real slots was written."""
+gathered hidden rows byte-exact.  Every K/V check covers the whole cache:
+small cases on the host against the oracle's assignment, the full-size
+configurations on the device (every real row against its source at the
+oracle's slot, every other row outside the null block against the sentinel)."""
 import numpy as np
 import pytest
 import torch
 
 import workloads
 from oracle import batch as ref_batch, cbind, step as ref_step, vectorised
-from tests.gpu_helpers import assert_step_equal, expected_step, read_rows_i32, replay_history
+from tests.gpu_helpers import assert_step_equal, check_cache_exact, expected_step, read_rows_i32, replay_history
+from workloads import payload_numpy
 from tests.oracle_helpers import golden
 
 pytestmark = pytest.mark.gpu
@@ -137,44 +138,99 @@ def test_kv_write_worked_example_full(rt):
     b.close()
 
 
-@pytest.mark.parametrize("name", ["decode_heavy", "mixed", "churn", "long_context"])
-def test_kv_write_full_size_sampled(rt, name):
-    """Full-size caches, every layer of the configuration, one launch: sampled
-    real tokens (plus every token of up to 2048) are compared with their source
-    rows at the oracle's slot, and sampled slots outside the step keep their
-    sentinel.  Decode-heavy and mixed take the wave-per-row shape, churn and
-    long-context chunk tiles."""
+@pytest.mark.parametrize("name", ["decode_heavy", "mixed", "churn", "long_context", "long_context_forced"])
+def test_kv_write_full_size(rt, name):
+    """Full-size caches, every layer of the configuration, one launch, every
+    byte: each real token's K and V rows equal their source rows at the
+    oracle's slot, and every cache row outside the step's real slots and the
+    null block still holds the sentinel (the rows holding anything else are
+    exactly the oracle's slot set), checked on the device.  Decode-heavy and
+    mixed take the wave-per-row shape, churn and long-context chunk tiles."""
     ric, runner = rt
     w = workloads.get(name)
     b, s, ref, order, exp, _ = _compile(rt, w)
     n_pad, N = exp["n_pad"], exp["num_actual_tokens"]
-    kc, vc = runner.alloc_caches(w, fill=0x1F2E)
+    sentinel = 0x1F2E
+    kc, vc = runner.alloc_caches(w, fill=sentinel)
     k, v = runner.alloc_sources(w, n_pad, seed=w.seed + 17)
     kv = runner.KVSet(k, v, kc, vc, w.row_bytes, w.num_kv_blocks * w.block_size)
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     runner.reshape_and_cache(kv, s.slot_mapping, n_pad, dev_status=status.data_ptr())
     torch.cuda.synchronize()
     assert int(status.item()) == 0
-    rng = np.random.default_rng(5)
-    toks = np.arange(N) if N <= 2048 else np.sort(rng.choice(N, 2048, replace=False))
-    slots = exp["slot_mapping"][toks]
-    real = set(exp["slot_mapping"][:N].tolist())
     B = w.block_size
     nslots = w.num_kv_blocks * B
-    free = rng.integers(B, nslots, size=4096)
-    free = np.array([x for x in free if int(x) not in real][:2048])
-    t_idx = torch.from_numpy(toks).cuda()
-    s_idx = torch.from_numpy(slots).cuda()
-    f_idx = torch.from_numpy(free).cuda()
+    null = (w.null_block * B, w.null_block * B + B)
     for l in range(w.num_layers):
-        for src, cache in ((k[l], kc[l]), (v[l], vc[l])):
-            flat = cache.view(torch.int16).reshape(nslots, -1)
-            srcf = src.view(torch.int16).reshape(n_pad, -1)
-            assert torch.equal(flat[s_idx], srcf[t_idx]), f"layer {l}: sampled rows differ"
-            assert bool((flat[f_idx] == 0x1F2E).all()), f"layer {l}: a slot outside the step was written"
+        for nm, src, cache in (("K", k[l], kc[l]), ("V", v[l], vc[l])):
+            check_cache_exact(cache, src, exp["slot_mapping"], N, sentinel, nslots, null, f"{name} layer {l} {nm}")
     del kc, vc, k, v, kv
     torch.cuda.empty_cache()
     b.close()
+
+
+# Row sizes and token counts that select each K/V launch shape: wave rows for
+# 1, 2 and 4 KiB rows up to 8192 tokens; chunk tiles otherwise (several rows
+# per workgroup below 4 KiB, one row per workgroup above, in one or several
+# passes; a chunk count per row that is not a power of two takes a division).
+KV_SHAPES = [
+    ("wave 1 KiB", 1024, 3000, 0),
+    ("wave 2 KiB", 2048, 777, 0),
+    ("wave 4 KiB", 4096, 5000, 0),
+    ("wave 4 KiB strided source", 4096, 1500, 4096 + 256),
+    ("wave 1 KiB at the token limit", 1024, 8192, 0),
+    ("chunk 1 KiB above the wave limit", 1024, 8193, 0),
+    ("chunk 4 KiB above the wave limit", 4096, 9000, 0),
+    ("chunk 8 KiB, two passes per row", 8192, 1200, 0),
+    ("chunk 12 KiB, three passes per row", 12288, 300, 0),
+    ("chunk 3 KiB, 192 chunks per row", 3072, 2000, 0),
+    ("chunk 48 B, division per chunk", 48, 4000, 64),
+    ("chunk 16 B", 16, 2500, 0),
+    ("chunk 256 B", 256, 3333, 0),
+]
+
+
+@pytest.mark.parametrize("label,row_bytes,n_tok,stride", KV_SHAPES, ids=[x[0] for x in KV_SHAPES])
+def test_kv_write_every_launch_shape(rt, label, row_bytes, n_tok, stride):
+    """Each K/V launch shape the library can pick, two layers in one launch,
+    distinct random slots in a cache of about twice the step: the whole cache
+    (every byte of every row) equals the oracle's fancy-index assignment into
+    a sentinel-filled copy."""
+    ric, runner = rt
+    rng = np.random.default_rng(row_bytes * 7919 + n_tok)
+    L = 2
+    num_slots = 2 * n_tok + 37
+    elems = row_bytes // 2
+    stride = stride or row_bytes
+    slots = rng.permutation(num_slots)[:n_tok].astype(np.int32)
+    sentinel = 0x6A6B
+    ks, vs, kcs, vcs, srcs = [], [], [], [], []
+    for l in range(L):
+        pair = []
+        for j in range(2):
+            base = payload_numpy(np.random.default_rng(1000 * l + j + row_bytes), (n_tok, stride // 2), "bf16")
+            pair.append(base)
+            t = torch.from_numpy(base.view(np.int16)).cuda()
+            (ks if j == 0 else vs).append(t)
+        srcs.append(pair)
+        for lst in (kcs, vcs):
+            lst.append(torch.full((num_slots, elems), sentinel, dtype=torch.int16, device="cuda"))
+    slot_t = torch.from_numpy(slots).cuda()
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ric.ric_reshape_and_cache([t.data_ptr() for t in ks], [t.data_ptr() for t in vs],
+                              [t.data_ptr() for t in kcs], [t.data_ptr() for t in vcs],
+                              slot_t.data_ptr(), n_tok, row_bytes, num_slots, src_row_stride=stride,
+                              dev_status=status.data_ptr(), stream=runner.current_stream())
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    for l in range(L):
+        k_np = srcs[l][0].view(np.int16)[:, :elems]
+        v_np = srcs[l][1].view(np.int16)[:, :elems]
+        want_k = np.full((num_slots, elems), sentinel, np.int16)
+        want_v = want_k.copy()
+        vectorised.reshape_and_cache(k_np, v_np, want_k, want_v, slots)
+        assert np.array_equal(kcs[l].cpu().numpy(), want_k), f"{label}: layer {l} K cache differs"
+        assert np.array_equal(vcs[l].cpu().numpy(), want_v), f"{label}: layer {l} V cache differs"
 
 
 @pytest.mark.parametrize("name", CONFIGS)

@@ -188,6 +188,42 @@ for step in range(600):
 check()
 ric.ric_destroy(h)
 
+# Uploads are refused while the stream is being captured, with nothing
+# changed; once the capture ends the same calls go through.
+cfg2 = ric.make_config(max_num_reqs=4, max_model_len=16, block_size=4, max_blocks_per_req=4,
+                       max_num_batched_tokens=16, num_kv_blocks=32, null_block=0, staging_bytes=0)
+h2 = ric.ric_create(cfg2, 0)
+ric.ric_add_request(h2, 4, [9], 1, 0, [5])
+ric.ric_add_request(h2, 5, [1, 2, 3, 4, 5], 5, 0, [3, 4])
+ric.ric_flush(h2)
+ric.ric_remove_request(h2, 4)                 # a hole at row 0
+ric.lib().fake_set_capturing(1)
+for fn, a in ((ric.ric_condense, (h2,)),):
+    try:
+        fn(*a)
+        raise AssertionError(f"{{fn.__name__}} uploaded during a capture")
+    except ric.RicError as e:
+        assert e.code == ric.RIC_ESTATE, (fn.__name__, e.code)
+ric.lib().fake_set_capturing(0)
+assert ric.ric_condense(h2) == 1 and ric.ric_row_of(h2, 5) == 0
+ric.ric_schedule(h2, [0], [5])
+ric.lib().fake_set_capturing(1)
+for fn, a in ((ric.ric_compile, (h2, 8)), (ric.ric_flush, (h2,)), (ric.ric_spec_decode_metadata, (h2, [0]))):
+    try:
+        fn(*a)
+        raise AssertionError(f"{{fn.__name__}} uploaded during a capture")
+    except ric.RicError as e:
+        assert e.code == ric.RIC_ESTATE, (fn.__name__, e.code)
+ric.lib().fake_set_capturing(0)
+s2 = ric.ric_compile(h2, 8)
+assert (s2.num_reqs, s2.num_actual_tokens) == (1, 5)
+cols2 = ric.ric_get_columns(h2)
+assert list(words(cols2.tokens, 5)) == [1, 2, 3, 4, 5] and list(words(cols2.num_scheduled, 1)) == [5]
+ric.lib().fake_set_capturing(1)
+s2 = ric.ric_compile(h2, 8)        # nothing staged: a capture may record the compile
+ric.lib().fake_set_capturing(0)
+ric.ric_destroy(h2)
+
 # The stateless entry points' argument checks (the fake device runs no kernels).
 def rejects(fn, *a, **kw):
     try:
@@ -222,6 +258,25 @@ for args in ((base, 64, 8, idx.ctypes.data, 0, 8, 40, base + 4096),     # row no
              (base, 64, -1, idx.ctypes.data, 0, 8, 64, base + 4096),    # negative source rows
              (base, 64, 8, idx.ctypes.data, 0, (1 << 24) + 1, 64, base + 4096)):
     assert rejects(g, *args) == ric.RIC_EINVAL, args
+# The slot-collision check: host argument checks, and the counts through the
+# device double.
+cs = ric.ric_check_slots
+nslots = 1000
+ws = np.zeros(ric.ric_check_slots_workspace_bytes(nslots) // 4, np.uint32)
+res = np.zeros(2, np.int32)
+sl = np.asarray([5, 7, 5, 999, 1000, -1, 7, 7], np.int32)
+cs(sl.ctypes.data, 8, nslots, ws.ctypes.data, ws.nbytes, res.ctypes.data)
+assert list(res) == [3, 2], list(res)
+cnt = np.asarray([3], np.int32)
+res[:] = 0
+cs(sl.ctypes.data, 8, nslots, ws.ctypes.data, ws.nbytes, res.ctypes.data, cnt.ctypes.data)
+assert list(res) == [1, 0], list(res)
+for args in ((sl.ctypes.data, 8, nslots, ws.ctypes.data, ws.nbytes - 256, res.ctypes.data),
+             (sl.ctypes.data, 8, 0, ws.ctypes.data, ws.nbytes, res.ctypes.data),
+             (sl.ctypes.data, (1 << 24) + 1, nslots, ws.ctypes.data, ws.nbytes, res.ctypes.data),
+             (sl.ctypes.data, 8, nslots, ws.ctypes.data + 2, ws.nbytes, res.ctypes.data),
+             (0, 8, nslots, ws.ctypes.data, ws.nbytes, res.ctypes.data)):
+    assert rejects(cs, *args) == ric.RIC_EINVAL, args
 print("sanitized control plane ok", next_id, "corrections", corrections)
 """
 
