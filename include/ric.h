@@ -425,6 +425,20 @@ int ric_check_slots(const int32_t* slot_mapping, int32_t num_tokens, const int32
                     int64_t num_slots, void* workspace, size_t workspace_bytes, int32_t* dev_result,
                     void* stream);
 
+/* ric_check_slots for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same check and counts, with the bitmap in a static device array of the
+ * library (4 MiB on each GPU it runs on, held until the process ends) instead
+ * of a workspace.  Runs on the current device.  Calls no allocator.  Every
+ * call on one GPU shares that GPU's bitmap, which each call clears (with a
+ * kernel) before use: calls that overlap on one GPU, on different streams or
+ * threads, race and must be serialised by the caller.
+ * Errors: ERANGE (num_slots above RIC_CHECK_SLOTS_NOALLOC_MAX_SLOTS), EINVAL,
+ * EHIP. */
+#define RIC_CHECK_SLOTS_NOALLOC_MAX_SLOTS (1LL << 25)
+int ric_check_slots_noalloc(const int32_t* slot_mapping, int32_t num_tokens, const int32_t* dev_num_tokens,
+                            int64_t num_slots, int32_t* dev_result, void* stream);
+
 /* ---- host-only helpers (no device work) ----------------------------------- */
 
 /* Smallest of the n capture sizes >= num_tokens; num_tokens itself when it

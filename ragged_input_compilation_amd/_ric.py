@@ -118,6 +118,7 @@ def _load():
         "ric_check_slots_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64]),
         "ric_check_slots": (ctypes.c_int, [_vp, ctypes.c_int32, _vp, ctypes.c_int64, _vp, ctypes.c_size_t, _vp,
                                            _vp]),
+        "ric_check_slots_noalloc": (ctypes.c_int, [_vp, ctypes.c_int32, _vp, ctypes.c_int64, _vp, _vp]),
         "ric_padded_size": (ctypes.c_int32, [_i32p, ctypes.c_int32, ctypes.c_int32]),
         "ric_condense_plan": (ctypes.c_int32, [_u8p, ctypes.c_int32, _i32p, _i32p]),
         "ric_check_step": (ctypes.c_int, [ctypes.POINTER(ric_config), ctypes.c_int32] + [_i32p] * 5 +
@@ -364,6 +365,12 @@ def ric_check_slots(slot_mapping: int, num_tokens: int, num_slots: int, workspac
     _err(_lib.ric_check_slots(_vp(slot_mapping or None), num_tokens, _vp(dev_num_tokens or None), num_slots,
                               _vp(workspace or None), workspace_bytes, _vp(dev_result or None),
                               _vp(stream or None)))
+
+
+def ric_check_slots_noalloc(slot_mapping: int, num_tokens: int, num_slots: int, dev_result: int,
+                            dev_num_tokens: int = 0, stream: int = 0) -> None:
+    _err(_lib.ric_check_slots_noalloc(_vp(slot_mapping or None), num_tokens, _vp(dev_num_tokens or None),
+                                      num_slots, _vp(dev_result or None), _vp(stream or None)))
 
 
 # ---- host-only helpers ----------------------------------------------------------

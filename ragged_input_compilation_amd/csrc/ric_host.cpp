@@ -1226,6 +1226,23 @@ int ric_check_slots(const int32_t* slot_mapping, int32_t num_tokens, const int32
     return RIC_OK;
 }
 
+int ric_check_slots_noalloc(const int32_t* slot_mapping, int32_t num_tokens, const int32_t* dev_num_tokens,
+                            int64_t num_slots, int32_t* dev_result, void* stream) {
+    if (num_tokens < 0 || num_tokens > kMaxRowsPerLaunch)
+        return fail(RIC_EINVAL, "num_tokens %d outside [0, %d]", num_tokens, kMaxRowsPerLaunch);
+    if (num_slots <= 0) return fail(RIC_EINVAL, "num_slots %lld must be positive", (long long)num_slots);
+    if (num_slots > kCheckScratchWords * 32)
+        return fail(RIC_ERANGE, "num_slots %lld above the %lld slots the library's static bitmap holds "
+                                "(use ric_check_slots with a workspace)", (long long)num_slots,
+                    (long long)(kCheckScratchWords * 32));
+    if (!dev_result || (num_tokens > 0 && !slot_mapping)) return fail(RIC_EINVAL, "NULL pointer argument");
+    uint32_t* bits = nullptr;
+    HIP_TRY(check_scratch_for_current_device(&bits));
+    HIP_TRY(launch_check_slots(slot_mapping, num_tokens, dev_num_tokens, num_slots, bits, dev_result,
+                               static_cast<hipStream_t>(stream)));
+    return RIC_OK;
+}
+
 int32_t ric_padded_size(const int32_t* sizes, int32_t n, int32_t num_tokens) {
     if (num_tokens < 0 || n < 0 || (n > 0 && !sizes)) return RIC_EINVAL;
     int32_t best = -1;

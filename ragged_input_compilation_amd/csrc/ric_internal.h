@@ -171,6 +171,14 @@ hipError_t launch_append_sampled(int32_t* tokens, const int64_t* dst_off, const 
 hipError_t launch_check_slots(const int32_t* slot, int32_t n, const int32_t* dev_n, int64_t num_slots,
                               uint32_t* bits, int32_t* result, hipStream_t s);
 
+// The allocation-free check keeps its bitmap in a static device array of
+// kCheckScratchWords words (4 MiB: up to 2^25 slots) on each GPU.
+constexpr int64_t kCheckScratchWords = int64_t(1) << 20;
+constexpr int kMaxScratchDevices = 64;
+// Device address of that array on the current device (looked up once per
+// device, then cached).
+hipError_t check_scratch_for_current_device(uint32_t** out);
+
 // Token tile of one compile workgroup.
 constexpr int kCompileThreads = 256;
 constexpr int kCompileTokensPerThread = 1;

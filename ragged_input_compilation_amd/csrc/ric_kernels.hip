@@ -14,6 +14,7 @@
 // vectors per lane, use non-temporal accesses where a byte is touched once per
 // step and the measurements favour them, and compute byte offsets in 64 bits.
 #include <algorithm>
+#include <mutex>
 
 #include "ric_internal.h"
 
@@ -715,6 +716,30 @@ __global__ __launch_bounds__(256) void mark_slots_kernel(const int32_t* slot, in
         const uint32_t m = 1u << (s & 31);
         if (atomicOr(bits + (s >> 5), m) & m) atomicAdd(result, 1);
     }
+}
+
+// Bitmap of the allocation-free variant: one copy per GPU, held until the
+// process ends.  Host code reaches it only through the address that
+// hipGetSymbolAddress returns for the current device (the array's name is a
+// host-side stand-in there, not a device address).
+static __device__ __align__(256) uint32_t scratch[kCheckScratchWords];
+
+hipError_t check_scratch_for_current_device(uint32_t** out) {
+    static std::mutex mu;
+    static uint32_t* ptr_of[kMaxScratchDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (ptr_of[dev] == nullptr) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        ptr_of[dev] = static_cast<uint32_t*>(ptr);
+    }
+    *out = ptr_of[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_check_slots(const int32_t* slot, int32_t n, const int32_t* dev_n, int64_t num_slots,

@@ -162,6 +162,12 @@ hipError_t launch_check_slots(const int32_t* slot, int32_t n, const int32_t* dev
     return hipSuccess;
 }
 
+hipError_t check_scratch_for_current_device(uint32_t** out) {
+    static std::vector<uint32_t> scratch_words((size_t)kCheckScratchWords);
+    *out = scratch_words.data();
+    return hipSuccess;
+}
+
 hipError_t launch_compile(const CompileParams&, hipStream_t) { return hipSuccess; }
 hipError_t launch_kv_scatter(const KVParams&, int, hipStream_t) { return hipSuccess; }
 hipError_t launch_gather(const GatherParams&, hipStream_t) { return hipSuccess; }
