@@ -369,6 +369,25 @@ int ric_schedule(ric_batch* b, int32_t num_reqs, const int32_t* num_computed,
  * N_pad > max_num_batched_tokens). */
 int ric_compile(ric_batch* b, int32_t num_tokens_padded, ric_step* out);
 
+/* ric_compile followed by ric_reshape_and_cache of the step's group-0 slot
+ * mapping over all num_tokens_padded tokens, on the handle's stream, with
+ * the same outputs and cache contents as those two calls
+ * ([P1 §3. 物理 KV 槽位], [P3 §实现]: each token's K/V row goes to the slot the
+ * compile gives it).  For rows of 1, 2 or 4 KiB the compile and the K/V write
+ * of up to 32 layers are one kernel: each workgroup derives its own tokens'
+ * slots and copies their rows, so there is no second launch to wait for;
+ * other row sizes and further layers use the separate K/V kernel after the
+ * compile.  The K/V arguments are those of ric_reshape_and_cache (k, v,
+ * k_cache, v_cache: host arrays of num_layers device pointers; src_row_stride
+ * 0 = row_bytes; dev_status optional; flags must be 0).  Padded tokens write
+ * their rows into the null block, as ric_reshape_and_cache does with the
+ * padded slot mapping.  Errors: those of ric_compile and of
+ * ric_reshape_and_cache; on an argument error nothing is enqueued. */
+int ric_compile_and_cache(ric_batch* b, int32_t num_tokens_padded, const void* const* k, const void* const* v,
+                          void* const* k_cache, void* const* v_cache, int32_t num_layers, int64_t src_row_stride,
+                          int32_t row_bytes, int64_t num_slots, int32_t* dev_status, uint32_t flags,
+                          ric_step* out);
+
 /* Write the step's new K/V rows into paged caches through a slot mapping
  * ([P1 §3. 物理 KV 槽位], [P3 §实现]: the t-th row goes to slot_mapping[t]).
  *   k[l], v[l]        host arrays of num_layers DEVICE pointers: source row t

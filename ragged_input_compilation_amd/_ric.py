@@ -110,6 +110,9 @@ def _load():
         "ric_read_device": (ctypes.c_int, [_vp, _vp, ctypes.c_size_t]),
         "ric_schedule": (ctypes.c_int, [_vp, ctypes.c_int32, _i32p, _i32p]),
         "ric_compile": (ctypes.c_int, [_vp, ctypes.c_int32, ctypes.POINTER(ric_step)]),
+        "ric_compile_and_cache": (ctypes.c_int, [_vp, ctypes.c_int32] + [ctypes.POINTER(_vp)] * 4 + [
+            ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int64, _vp, ctypes.c_uint32,
+            ctypes.POINTER(ric_step)]),
         "ric_reshape_and_cache": (ctypes.c_int, [ctypes.POINTER(_vp)] * 4 + [
             ctypes.c_int32, _vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int64, _vp,
             ctypes.c_uint32, _vp]),
@@ -333,6 +336,24 @@ def ric_schedule(h: int, num_computed, num_scheduled) -> None:
 def ric_compile(h: int, num_tokens_padded: int) -> ric_step:
     s = ric_step()
     _err(_lib.ric_compile(_vp(h), num_tokens_padded, ctypes.byref(s)))
+    return s
+
+
+def _ptr_arrays(k_ptrs, v_ptrs, k_cache_ptrs, v_cache_ptrs):
+    L = len(k_ptrs)
+    if not (len(v_ptrs) == len(k_cache_ptrs) == len(v_cache_ptrs) == L):
+        raise ValueError("pointer lists differ in length")
+    arr = [(_vp * max(L, 1))(*[_vp(p) for p in lst]) for lst in (k_ptrs, v_ptrs, k_cache_ptrs, v_cache_ptrs)]
+    return L, arr, [ctypes.cast(a, ctypes.POINTER(_vp)) for a in arr]
+
+
+def ric_compile_and_cache(h: int, num_tokens_padded: int, k_ptrs, v_ptrs, k_cache_ptrs, v_cache_ptrs,
+                          row_bytes: int, num_slots: int, src_row_stride: int = 0, dev_status: int = 0,
+                          flags: int = 0) -> ric_step:
+    L, keep, ptrs = _ptr_arrays(k_ptrs, v_ptrs, k_cache_ptrs, v_cache_ptrs)
+    s = ric_step()
+    _err(_lib.ric_compile_and_cache(_vp(h), num_tokens_padded, *ptrs, L, src_row_stride, row_bytes, num_slots,
+                                    _vp(dev_status or None), flags, ctypes.byref(s)))
     return s
 
 

@@ -1055,15 +1055,11 @@ int ric_schedule(ric_batch* b, int32_t R, const int32_t* c, const int32_t* q) {
     return RIC_OK;
 }
 
-int ric_compile(ric_batch* b, int32_t n_pad, ric_step* out) {
-    if (!b) return fail(RIC_EINVAL, "handle is NULL");
-    DeviceScope ds(b);
-    if (!b->scheduled) return fail(RIC_ESTATE, "ric_schedule must follow the last row change");
-    if (n_pad < b->sched_N || n_pad > b->cfg.max_num_batched_tokens)
-        return fail(RIC_EINVAL, "num_tokens_padded %d outside [N=%d, max_num_batched_tokens=%d]", n_pad,
-                    b->sched_N, b->cfg.max_num_batched_tokens);
-    int rc = flush(b);
-    if (rc) return rc;
+}  // extern "C"
+
+namespace {
+
+CompileParams compile_params(ric_batch* b, int32_t n_pad) {
     CompileParams p{};
     p.scal = b->d_scal;
     p.tokens = b->d_tok;
@@ -1100,45 +1096,53 @@ int ric_compile(ric_batch* b, int32_t n_pad, ric_step* out) {
         p.xnull_slot[x] = b->cfg.null_block * B;
         p.xslot_mapping[x] = b->d_xslot[g];
     }
-    HIP_TRY(launch_compile(p, b->stream));
-    b->compiled = true;
-    if (out) {
-        out->input_ids = b->d_ids;
-        out->positions = b->d_pos;
-        out->req_indices = b->d_req;
-        out->slot_mapping = b->d_slot;
-        out->query_start_loc = b->d_qsl;
-        out->seq_lens = b->d_seq;
-        out->logits_indices = b->d_logits;
-        out->discard = b->d_discard;
-        out->sample_indices = b->d_sample;
-        out->dev_scalars = b->d_dscal;
-        out->cu_seqlens_k = b->d_cuk;
-        for (int g = 0; g < RIC_MAX_KV_GROUPS; ++g)
-            out->group_slot_mapping[g] = (g == 0) ? b->d_slot : (g < b->L.groups ? b->d_xslot[g] : nullptr);
-        out->num_reqs = b->sched_R;
-        out->num_actual_tokens = b->sched_N;
-        out->num_tokens_padded = n_pad;
-        out->max_query_len = b->sched_max_q;
-        out->max_seq_len = b->sched_max_seq;
-        out->num_sampled = b->sched_sampled;
-    }
+    return p;
+}
+
+void fill_step(const ric_batch* b, int32_t n_pad, ric_step* out) {
+    if (!out) return;
+    out->input_ids = b->d_ids;
+    out->positions = b->d_pos;
+    out->req_indices = b->d_req;
+    out->slot_mapping = b->d_slot;
+    out->query_start_loc = b->d_qsl;
+    out->seq_lens = b->d_seq;
+    out->logits_indices = b->d_logits;
+    out->discard = b->d_discard;
+    out->sample_indices = b->d_sample;
+    out->dev_scalars = b->d_dscal;
+    out->cu_seqlens_k = b->d_cuk;
+    for (int g = 0; g < RIC_MAX_KV_GROUPS; ++g)
+        out->group_slot_mapping[g] = (g == 0) ? b->d_slot : (g < b->L.groups ? b->d_xslot[g] : nullptr);
+    out->num_reqs = b->sched_R;
+    out->num_actual_tokens = b->sched_N;
+    out->num_tokens_padded = n_pad;
+    out->max_query_len = b->sched_max_q;
+    out->max_seq_len = b->sched_max_seq;
+    out->num_sampled = b->sched_sampled;
+}
+
+int check_compile_args(const ric_batch* b, int32_t n_pad) {
+    if (!b->scheduled) return fail(RIC_ESTATE, "ric_schedule must follow the last row change");
+    if (n_pad < b->sched_N || n_pad > b->cfg.max_num_batched_tokens)
+        return fail(RIC_EINVAL, "num_tokens_padded %d outside [N=%d, max_num_batched_tokens=%d]", n_pad,
+                    b->sched_N, b->cfg.max_num_batched_tokens);
     return RIC_OK;
 }
 
-static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-int ric_reshape_and_cache(const void* const* k, const void* const* v, void* const* k_cache, void* const* v_cache,
-                          int32_t num_layers, const int32_t* slot_mapping, int32_t num_tokens,
-                          int64_t src_row_stride, int32_t row_bytes, int64_t num_slots, int32_t* dev_status,
-                          uint32_t flags, void* stream) {
+// Argument checks shared by the K/V-writing calls; fills the launch
+// parameters that do not depend on the layer range.
+int kv_params(const void* const* k, const void* const* v, void* const* k_cache, void* const* v_cache,
+              int32_t num_layers, int32_t num_tokens, int64_t src_row_stride, int32_t row_bytes, int64_t num_slots,
+              int32_t* dev_status, uint32_t flags, KVParams* p) {
     if (num_layers < 0 || num_tokens < 0) return fail(RIC_EINVAL, "negative count");
     if (flags != 0) return fail(RIC_EINVAL, "flags 0x%x: no flag is defined (pass 0)", flags);
-    if (num_layers == 0 || num_tokens == 0) return RIC_OK;
     if (num_tokens > kMaxRowsPerLaunch)
         return fail(RIC_EINVAL, "num_tokens %d above %d per call (the grid counts work-items in 32 bits)",
                     num_tokens, kMaxRowsPerLaunch);
-    if (!k || !v || !k_cache || !v_cache || !slot_mapping) return fail(RIC_EINVAL, "NULL pointer argument");
+    if (num_layers > 0 && (!k || !v || !k_cache || !v_cache)) return fail(RIC_EINVAL, "NULL pointer argument");
     if (row_bytes <= 0 || row_bytes % 16 != 0) return fail(RIC_EINVAL, "row_bytes %d not a positive multiple of 16", row_bytes);
     if (src_row_stride == 0) src_row_stride = row_bytes;
     if (src_row_stride < row_bytes || src_row_stride % 16 != 0)
@@ -1148,24 +1152,97 @@ int ric_reshape_and_cache(const void* const* k, const void* const* v, void* cons
         if (!k[l] || !v[l] || !k_cache[l] || !v_cache[l] || !aligned16(k[l]) || !aligned16(v[l]) ||
             !aligned16(k_cache[l]) || !aligned16(v_cache[l]))
             return fail(RIC_EINVAL, "layer %d: NULL or misaligned pointer", l);
+    *p = KVParams{};
+    p->src_stride = src_row_stride;
+    p->num_slots = num_slots;
+    p->status = dev_status;
+    p->num_tokens = num_tokens;
+    p->row_bytes = row_bytes;
+    p->chunk_shift = ilog2_exact(row_bytes / 16);
+    p->rows_per_wg = 0;
+    return RIC_OK;
+}
+
+void set_layers(KVParams* p, const void* const* k, const void* const* v, void* const* k_cache, void* const* v_cache,
+                int32_t l0, int nl) {
+    for (int i = 0; i < nl; ++i) {
+        p->k[i] = static_cast<const uint8_t*>(k[l0 + i]);
+        p->v[i] = static_cast<const uint8_t*>(v[l0 + i]);
+        p->kc[i] = static_cast<uint8_t*>(k_cache[l0 + i]);
+        p->vc[i] = static_cast<uint8_t*>(v_cache[l0 + i]);
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+int ric_compile(ric_batch* b, int32_t n_pad, ric_step* out) {
+    if (!b) return fail(RIC_EINVAL, "handle is NULL");
+    DeviceScope ds(b);
+    int rc = check_compile_args(b, n_pad);
+    if (rc) return rc;
+    rc = flush(b);
+    if (rc) return rc;
+    HIP_TRY(launch_compile(compile_params(b, n_pad), b->stream));
+    b->compiled = true;
+    fill_step(b, n_pad, out);
+    return RIC_OK;
+}
+
+int ric_compile_and_cache(ric_batch* b, int32_t n_pad, const void* const* k, const void* const* v,
+                          void* const* k_cache, void* const* v_cache, int32_t num_layers, int64_t src_row_stride,
+                          int32_t row_bytes, int64_t num_slots, int32_t* dev_status, uint32_t flags,
+                          ric_step* out) {
+    if (!b) return fail(RIC_EINVAL, "handle is NULL");
+    DeviceScope ds(b);
+    int rc = check_compile_args(b, n_pad);
+    if (rc) return rc;
+    KVParams kv{};
+    rc = kv_params(k, v, k_cache, v_cache, num_layers, n_pad, src_row_stride, row_bytes, num_slots, dev_status,
+                   flags, &kv);
+    if (rc) return rc;
+    rc = flush(b);
+    if (rc) return rc;
+    const CompileParams p = compile_params(b, n_pad);
+    kv.slot = b->d_slot;
+    int32_t done = 0;
+    if (num_layers > 0 && n_pad > 0 && fused_kv_supported(row_bytes)) {
+        done = std::min<int32_t>(kMaxLayersPerLaunch, num_layers);
+        set_layers(&kv, k, v, k_cache, v_cache, 0, done);
+        HIP_TRY(launch_compile_kv(p, kv, done, b->stream));
+    } else {
+        HIP_TRY(launch_compile(p, b->stream));
+    }
+    // Layers past the first launch, or rows the fused kernel does not take:
+    // the K/V kernels through the slot mapping just written.
+    for (int32_t l0 = done; l0 < num_layers && n_pad > 0; l0 += kMaxLayersPerLaunch) {
+        const int nl = std::min<int>(kMaxLayersPerLaunch, num_layers - l0);
+        set_layers(&kv, k, v, k_cache, v_cache, l0, nl);
+        HIP_TRY(launch_kv_scatter(kv, nl, b->stream));
+    }
+    b->compiled = true;
+    fill_step(b, n_pad, out);
+    return RIC_OK;
+}
+
+int ric_reshape_and_cache(const void* const* k, const void* const* v, void* const* k_cache, void* const* v_cache,
+                          int32_t num_layers, const int32_t* slot_mapping, int32_t num_tokens,
+                          int64_t src_row_stride, int32_t row_bytes, int64_t num_slots, int32_t* dev_status,
+                          uint32_t flags, void* stream) {
+    if (num_layers < 0 || num_tokens < 0) return fail(RIC_EINVAL, "negative count");
+    if (flags != 0) return fail(RIC_EINVAL, "flags 0x%x: no flag is defined (pass 0)", flags);
+    if (num_layers == 0 || num_tokens == 0) return RIC_OK;
+    if (!slot_mapping) return fail(RIC_EINVAL, "NULL pointer argument");
     KVParams p{};
+    int rc = kv_params(k, v, k_cache, v_cache, num_layers, num_tokens, src_row_stride, row_bytes, num_slots,
+                       dev_status, flags, &p);
+    if (rc) return rc;
     p.slot = slot_mapping;
-    p.src_stride = src_row_stride;
-    p.num_slots = num_slots;
-    p.status = dev_status;
-    p.num_tokens = num_tokens;
-    p.row_bytes = row_bytes;
-    p.chunk_shift = ilog2_exact(row_bytes / 16);
-    p.rows_per_wg = 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
     for (int32_t l0 = 0; l0 < num_layers; l0 += kMaxLayersPerLaunch) {
         const int nl = std::min<int>(kMaxLayersPerLaunch, num_layers - l0);
-        for (int i = 0; i < nl; ++i) {
-            p.k[i] = static_cast<const uint8_t*>(k[l0 + i]);
-            p.v[i] = static_cast<const uint8_t*>(v[l0 + i]);
-            p.kc[i] = static_cast<uint8_t*>(k_cache[l0 + i]);
-            p.vc[i] = static_cast<uint8_t*>(v_cache[l0 + i]);
-        }
+        set_layers(&p, k, v, k_cache, v_cache, l0, nl);
         HIP_TRY(launch_kv_scatter(p, nl, s));
     }
     return RIC_OK;

@@ -137,141 +137,173 @@ __device__ __forceinline__ void block_scan2_max2(int a[2], int m[2], int* tmp, i
 //   slot: block_table[i][p / B] * B + p % B          [P1 §Block table 是逐请求的页表]
 //   logits index: qsl[i+1] - 1; partial prefills discarded  [P1 §第四步], [P1 §Chunked Prefill]
 //   padded tokens -> null block                      [P1 §固定地址与动态有效长度如何共存], [P4 §5]
+// The three parts below are shared by the compile kernel and the fused
+// compile + K/V kernel, so both produce the same outputs by construction.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kCompileThreads) void compile_kernel(CompileParams p) {
-    extern __shared__ int32_t smem[];
-    const int R = p.num_reqs;
-    int32_t* s_qsl = smem;               // [R + 1]
-    int32_t* s_base = smem + R + 1;      // [R]: c_i - qsl_i, so position = base + t
-    int32_t* s_tmp = s_base + R;         // [kCompileThreads / kWave]
-    int32_t* s_red = s_tmp + kCompileThreads / kWave;   // [4 * kCompileThreads / kWave]
 
+// LDS of one compile workgroup: query_start_loc [R + 1], base [R] (c_i - qsl_i,
+// so that position = base + t), one scan word per wave, four reduction words
+// per wave.
+struct CompileLds {
+    int32_t* qsl;
+    int32_t* base;
+    int32_t* tmp;
+    int32_t* red;
+    __device__ CompileLds(int32_t* smem, int R)
+        : qsl(smem), base(smem + R + 1), tmp(smem + 2 * R + 1), red(smem + 2 * R + 1 + kCompileThreads / kWave) {}
+    static constexpr int extra_words = 5 * kCompileThreads / kWave;
+};
+
+// What a thread of the per-request workgroup carries from the scan to the
+// per-request outputs: its contiguous run of requests [r0, r1) and their
+// partial sums and maxima.
+struct ReqRun {
+    int r0, r1;
+    int kept, max_q, max_seq, local_seq;
+    uint32_t partial;   // bit k: request r0 + k has not reached the end of its prompt
+};
+
+// Rebuilds query_start_loc and the position bases in LDS; returns N.  Each
+// thread owns a contiguous run of at most 32 requests (R <= 8000).  A
+// request's q and c (and, in the per-request workgroup, its prompt length) are
+// loaded together; up to 256 requests that is one round trip per thread.
+// Above that the loop takes a thread's requests one after another: issuing
+// four at a time measured the same (1024 requests), and all at once (unrolled
+// and predicated: larger code) about 1 us slower per compile.  Contains
+// barriers: every thread of the workgroup must call it.
+__device__ __forceinline__ int scan_requests(const CompileParams& p, const CompileLds& L, bool req_wg, ReqRun& run) {
+    const int R = p.num_reqs;
     const int tid = threadIdx.x;
     const int32_t* col_c = p.scal + (int64_t)kNumComputed * p.max_num_reqs;
     const int32_t* col_q = p.scal + (int64_t)kNumScheduled * p.max_num_reqs;
     const int32_t* col_P = p.scal + (int64_t)kNumPrompt * p.max_num_reqs;
-
-    // Each thread owns a contiguous run of at most 32 requests (R <= 8000).
-    // A request's q and c (and, in the per-request workgroup, its prompt
-    // length) are loaded together; up to 256 requests that is one round trip
-    // per thread.  Above that the loop takes a thread's requests one after
-    // another: issuing four at a time measured the same (1024 requests), and
-    // all at once (unrolled and predicated: larger code) about 1 us slower
-    // per compile.
-    const bool req_wg = (int)blockIdx.x >= p.num_token_tiles;
     const int per = (R + kCompileThreads - 1) / kCompileThreads;
-    const int r0 = min(R, tid * per);
-    const int r1 = min(R, r0 + per);
-    int local = 0, kept = 0, max_q = 0, max_seq = 0, local_seq = 0;
-    uint32_t partial = 0;   // bit k: request r0 + k has not reached the end of its prompt
-    for (int i = r0; i < r1; ++i) {
+    run.r0 = min(R, tid * per);
+    run.r1 = min(R, run.r0 + per);
+    run.kept = 0;
+    run.max_q = 0;
+    run.max_seq = 0;
+    run.local_seq = 0;
+    run.partial = 0;
+    int local = 0;
+    for (int i = run.r0; i < run.r1; ++i) {
         const int q = col_q[i];
         const int c = col_c[i];
-        s_qsl[i] = q;
-        s_base[i] = c;
+        L.qsl[i] = q;
+        L.base[i] = c;
         local += q;
         if (req_wg) {
             const int seq = c + q;
             const bool part = seq < col_P[i];
-            partial |= (part ? 1u : 0u) << (i - r0);
-            kept += part ? 0 : 1;
-            max_q = max(max_q, q);
-            max_seq = max(max_seq, seq);
-            local_seq += seq;
+            run.partial |= (part ? 1u : 0u) << (i - run.r0);
+            run.kept += part ? 0 : 1;
+            run.max_q = max(run.max_q, q);
+            run.max_seq = max(run.max_seq, seq);
+            run.local_seq += seq;
         }
     }
     int N = 0;
-    int run = block_exclusive_scan<kCompileThreads>(local, s_tmp, &N);
-    for (int i = r0; i < r1; ++i) {
-        const int q = s_qsl[i];
-        s_qsl[i] = run;
-        s_base[i] -= run;
-        run += q;
+    int off = block_exclusive_scan<kCompileThreads>(local, L.tmp, &N);
+    for (int i = run.r0; i < run.r1; ++i) {
+        const int q = L.qsl[i];
+        L.qsl[i] = off;
+        L.base[i] -= off;
+        off += q;
     }
-    if (tid == 0) s_qsl[R] = N;
+    if (tid == 0) L.qsl[R] = N;
     __syncthreads();
+    return N;
+}
 
-    if ((int)blockIdx.x < p.num_token_tiles) {
-        const int tile0 = blockIdx.x * kCompileTile;
-#pragma unroll
-        for (int k = 0; k < kCompileTokensPerThread; ++k) {
-            const int t = tile0 + k * kCompileThreads + tid;
-            if (t >= p.n_pad) break;
-            if (t < N) {
-                // request r: the last one whose interval starts at or before t
-                int lo = 0, hi = R - 1;
-                while (lo < hi) {
-                    const int mid = (lo + hi + 1) >> 1;
-                    if (s_qsl[mid] <= t) lo = mid; else hi = mid - 1;
-                }
-                const int r = lo;
-                const int pos = s_base[r] + t;
-                int lb, off;
-                if (p.block_shift >= 0) {
-                    lb = pos >> p.block_shift;
-                    off = pos & (p.block_size - 1);
-                } else {
-                    lb = pos / p.block_size;
-                    off = pos - lb * p.block_size;
-                }
-                p.positions[t] = pos;
-                p.req_indices[t] = r;
-                // The host validated c + q <= T and the block count; this guard
-                // only keeps a corrupted column from turning into a wild read.
-                if (pos >= 0 && pos < p.tok_stride && lb < p.blk_stride) {
-                    p.input_ids[t] = p.tokens[(int64_t)r * p.tok_stride + pos];
-                    p.slot_mapping[t] = p.blocks[(int64_t)r * p.blk_stride + lb] * p.block_size + off;
-                } else {
-                    p.input_ids[t] = -1;
-                    p.slot_mapping[t] = p.null_slot;
-                    atomicAdd(p.dev_scalars + 6, 1);
-                }
-                // Further KV-cache groups: the same position through each
-                // group's own block table and block size ([P1 §混合 KV Cache：
-                // 一条请求不止一张页表]).
-                for (int x = 0; x < p.num_extra_groups; ++x) {
-                    const int B = p.xblock_size[x];
-                    int xlb, xoff;
-                    if (p.xblock_shift[x] >= 0) {
-                        xlb = pos >> p.xblock_shift[x];
-                        xoff = pos & (B - 1);
-                    } else {
-                        xlb = pos / B;
-                        xoff = pos - xlb * B;
-                    }
-                    if (pos >= 0 && xlb < p.xblk_stride[x]) {
-                        p.xslot_mapping[x][t] = p.xblocks[x][(int64_t)r * p.xblk_stride[x] + xlb] * B + xoff;
-                    } else {
-                        p.xslot_mapping[x][t] = p.xnull_slot[x];
-                        atomicAdd(p.dev_scalars + 6, 1);
-                    }
-                }
-            } else {
-                p.input_ids[t] = 0;
-                p.positions[t] = 0;
-                p.req_indices[t] = -1;
-                p.slot_mapping[t] = p.null_slot;
-                for (int x = 0; x < p.num_extra_groups; ++x) p.xslot_mapping[x][t] = p.xnull_slot[x];
-            }
+// Token t < n_pad: its group-0 slot; with `write`, also its per-token outputs
+// (input id, position, request, slots of every slotted group).
+__device__ __forceinline__ int token_outputs(const CompileParams& p, const CompileLds& L, int N, int t, bool write) {
+    const int R = p.num_reqs;
+    if (t >= N) {
+        if (write) {
+            p.input_ids[t] = 0;
+            p.positions[t] = 0;
+            p.req_indices[t] = -1;
+            p.slot_mapping[t] = p.null_slot;
+            for (int x = 0; x < p.num_extra_groups; ++x) p.xslot_mapping[x][t] = p.xnull_slot[x];
         }
-        return;
+        return p.null_slot;
     }
+    // request r: the last one whose interval starts at or before t
+    int lo = 0, hi = R - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (L.qsl[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    const int r = lo;
+    const int pos = L.base[r] + t;
+    int lb, off;
+    if (p.block_shift >= 0) {
+        lb = pos >> p.block_shift;
+        off = pos & (p.block_size - 1);
+    } else {
+        lb = pos / p.block_size;
+        off = pos - lb * p.block_size;
+    }
+    int slot;
+    // The host validated c + q <= T and the block count; this guard only
+    // keeps a corrupted column from turning into a wild read.
+    const bool ok = pos >= 0 && pos < p.tok_stride && lb < p.blk_stride;
+    if (ok) {
+        slot = p.blocks[(int64_t)r * p.blk_stride + lb] * p.block_size + off;
+    } else {
+        slot = p.null_slot;
+    }
+    if (!write) return slot;
+    p.positions[t] = pos;
+    p.req_indices[t] = r;
+    if (ok) {
+        p.input_ids[t] = p.tokens[(int64_t)r * p.tok_stride + pos];
+        p.slot_mapping[t] = slot;
+    } else {
+        p.input_ids[t] = -1;
+        p.slot_mapping[t] = p.null_slot;
+        atomicAdd(p.dev_scalars + 6, 1);
+    }
+    // Further KV-cache groups: the same position through each group's own
+    // block table and block size ([P1 §混合 KV Cache：一条请求不止一张页表]).
+    for (int x = 0; x < p.num_extra_groups; ++x) {
+        const int B = p.xblock_size[x];
+        int xlb, xoff;
+        if (p.xblock_shift[x] >= 0) {
+            xlb = pos >> p.xblock_shift[x];
+            xoff = pos & (B - 1);
+        } else {
+            xlb = pos / B;
+            xoff = pos - xlb * B;
+        }
+        if (pos >= 0 && xlb < p.xblk_stride[x]) {
+            p.xslot_mapping[x][t] = p.xblocks[x][(int64_t)r * p.xblk_stride[x] + xlb] * B + xoff;
+        } else {
+            p.xslot_mapping[x][t] = p.xnull_slot[x];
+            atomicAdd(p.dev_scalars + 6, 1);
+        }
+    }
+    return slot;
+}
 
-    // Per-request outputs (one workgroup).
+// Per-request outputs, written by one workgroup: compacted-sample positions,
+// and the key-side boundaries of a varlen attention call (running total of
+// seq_lens), in one pass with the maxima.  Contains a barrier: every thread of
+// the workgroup must call it.
+__device__ __forceinline__ void request_outputs(const CompileParams& p, const ReqRun& run, const CompileLds& L, int N) {
+    const int R = p.num_reqs;
     const int MR = p.max_num_reqs;
-    // compacted-sample positions, and the key-side boundaries of a varlen
-    // attention call (running total of seq_lens), in one pass with the maxima
-    int sc[2] = {kept, local_seq}, mx[2] = {max_q, max_seq}, tot[2];
-    block_scan2_max2<kCompileThreads>(sc, mx, s_red, tot);
+    const int tid = threadIdx.x;
+    int sc[2] = {run.kept, run.local_seq}, mx[2] = {run.max_q, run.max_seq}, tot[2];
+    block_scan2_max2<kCompileThreads>(sc, mx, L.red, tot);
     int slot_out = sc[0], seq_run = sc[1];
     const int num_sampled = tot[0], seq_total = tot[1];
-    max_q = mx[0];
-    max_seq = mx[1];
-    for (int i = r0; i < r1; ++i) {
-        const int end = s_qsl[i + 1];
+    for (int i = run.r0; i < run.r1; ++i) {
+        const int end = L.qsl[i + 1];
         const int li = end - 1;
-        const int seq = s_base[i] + end;   // c_i + q_i
-        const bool part = ((partial >> (i - r0)) & 1u) != 0;
+        const int seq = L.base[i] + end;   // c_i + q_i
+        const bool part = ((run.partial >> (i - run.r0)) & 1u) != 0;
         p.seq_lens[i] = seq;
         p.cu_seqlens_k[i] = seq_run;
         seq_run += seq;
@@ -280,7 +312,7 @@ __global__ __launch_bounds__(kCompileThreads) void compile_kernel(CompileParams 
         if (!part) p.sample_indices[slot_out++] = li;
     }
     for (int i = tid; i <= MR; i += kCompileThreads) {
-        p.query_start_loc[i] = (i <= R) ? s_qsl[i] : N;
+        p.query_start_loc[i] = (i <= R) ? L.qsl[i] : N;
         if (i >= R) p.cu_seqlens_k[i] = seq_total;
         if (i >= R && i < MR) {
             p.seq_lens[i] = 0;
@@ -293,15 +325,38 @@ __global__ __launch_bounds__(kCompileThreads) void compile_kernel(CompileParams 
         p.dev_scalars[0] = R;
         p.dev_scalars[1] = N;
         p.dev_scalars[2] = p.n_pad;
-        p.dev_scalars[3] = max_q;
-        p.dev_scalars[4] = max_seq;
+        p.dev_scalars[3] = mx[0];
+        p.dev_scalars[4] = mx[1];
         p.dev_scalars[5] = num_sampled;
     }
 }
 
+__global__ __launch_bounds__(kCompileThreads) void compile_kernel(CompileParams p) {
+    extern __shared__ int32_t smem[];
+    const CompileLds L(smem, p.num_reqs);
+    const bool req_wg = (int)blockIdx.x >= p.num_token_tiles;
+    ReqRun run;
+    const int N = scan_requests(p, L, req_wg, run);
+    if (!req_wg) {
+        const int tile0 = blockIdx.x * kCompileTile;
+#pragma unroll
+        for (int k = 0; k < kCompileTokensPerThread; ++k) {
+            const int t = tile0 + k * kCompileThreads + threadIdx.x;
+            if (t >= p.n_pad) break;
+            token_outputs(p, L, N, t, true);
+        }
+        return;
+    }
+    request_outputs(p, run, L, N);
+}
+
+static size_t compile_lds_bytes(int num_reqs, int extra_words) {
+    return sizeof(int32_t) * (2 * (size_t)num_reqs + 1 + CompileLds::extra_words + extra_words);
+}
+
 hipError_t launch_compile(const CompileParams& p, hipStream_t s) {
-    const size_t lds = sizeof(int32_t) * (2 * (size_t)p.num_reqs + 1 + 5 * (kCompileThreads / kWave));
-    hipLaunchKernelGGL(compile_kernel, dim3(p.num_token_tiles + 1), dim3(kCompileThreads), lds, s, p);
+    hipLaunchKernelGGL(compile_kernel, dim3(p.num_token_tiles + 1), dim3(kCompileThreads),
+                       compile_lds_bytes(p.num_reqs, 0), s, p);
     return hipGetLastError();
 }
 
@@ -443,6 +498,105 @@ hipError_t launch_kv_scatter(const KVParams& p_in, int num_layers, hipStream_t s
     p.rows_per_wg = p.rows_per_wg > 0 ? p.rows_per_wg : max(1, kKvTileBytes / p.row_bytes);
     const int gx = (p.num_tokens + p.rows_per_wg - 1) / p.rows_per_wg;
     hipLaunchKernelGGL((kv_chunk_kernel<1, true, true>), dim3(gx, 2 * num_layers), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Compile and K/V write in one launch.  blockIdx.y = layer; workgroup x <
+// num_token_tiles owns TT = ROWS * 4 consecutive tokens, the last one (layer 0
+// only) writes the per-request outputs.  Each token workgroup rebuilds
+// query_start_loc in LDS like the compile kernel, derives its tokens' slots
+// (layer-0 workgroups also write the per-token outputs) and copies its
+// tokens' K and V rows of its layer to those slots, wave by wave as the wave
+// kernel does.  This saves the second launch and the drain between the two
+// kernels, and lets the K/V copy of one tile overlap the slot work of
+// another.  With LOADS_FIRST the source rows are loaded before the prefix
+// sum (they do not depend on it).  A slot outside [0, num_slots) skips its
+// row and counts in *status, as in the K/V kernels.
+// ---------------------------------------------------------------------------
+template <int CPL, int ROWS, bool LOADS_FIRST>
+__global__ __launch_bounds__(kCompileThreads) void compile_kv_kernel(CompileParams p, KVParams kv) {
+    constexpr int WAVES = kCompileThreads / kWave;
+    constexpr int TT = ROWS * WAVES;
+    extern __shared__ int32_t smem[];
+    const CompileLds L(smem, p.num_reqs);
+    int32_t* s_slot = smem + 2 * p.num_reqs + 1 + CompileLds::extra_words;   // [TT]
+    const int layer = blockIdx.y;
+    const bool req_wg = (int)blockIdx.x >= p.num_token_tiles;
+    if (req_wg && layer != 0) return;          // whole workgroup: before any barrier
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tile0 = blockIdx.x * TT;
+    const int t0 = tile0 + wid * ROWS;         // this wave's first row
+    const uint8_t* __restrict__ ks = kv.k[layer];
+    const uint8_t* __restrict__ vs = kv.v[layer];
+    u32x4 a[ROWS][2 * CPL];
+    auto load_rows = [&]() {
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+            const int t = t0 + r;
+            if (t < p.n_pad) {
+                const int64_t so = (int64_t)t * kv.src_stride + lane * 16;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    a[r][c] = load16<true>(ks + so + c * 1024);
+                    a[r][CPL + c] = load16<true>(vs + so + c * 1024);
+                }
+            }
+        }
+    };
+    if (LOADS_FIRST && !req_wg) load_rows();
+    ReqRun run;
+    const int N = scan_requests(p, L, req_wg, run);
+    if (req_wg) {
+        request_outputs(p, run, L, N);
+        return;
+    }
+    if ((int)threadIdx.x < TT) {
+        const int t = tile0 + threadIdx.x;
+        if (t < p.n_pad) s_slot[threadIdx.x] = token_outputs(p, L, N, t, layer == 0);
+    }
+    __syncthreads();
+    if (!LOADS_FIRST) load_rows();
+    uint8_t* __restrict__ kd = kv.kc[layer];
+    uint8_t* __restrict__ vd = kv.vc[layer];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+        const int t = t0 + r;
+        if (t >= p.n_pad) break;
+        const int s = s_slot[wid * ROWS + r];
+        if (s >= 0 && (int64_t)s < kv.num_slots) {
+            const int64_t off = (int64_t)s * kv.row_bytes + lane * 16;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                store16<true>(kd + off + c * 1024, a[r][c]);
+                store16<true>(vd + off + c * 1024, a[r][CPL + c]);
+            }
+        } else if (lane == 0 && kv.status != nullptr) {
+            atomicAdd(kv.status, 2);
+        }
+    }
+}
+
+constexpr int kFusedRows = 4;
+constexpr bool kFusedLoadsFirst = true;
+
+bool fused_kv_supported(int row_bytes) { return row_bytes == 1024 || row_bytes == 2048 || row_bytes == 4096; }
+
+template <int CPL>
+static void launch_fused(const CompileParams& p_in, const KVParams& kv, int num_layers, hipStream_t s) {
+    constexpr int TT = kFusedRows * (kCompileThreads / kWave);
+    CompileParams p = p_in;
+    p.num_token_tiles = (p.n_pad + TT - 1) / TT;
+    hipLaunchKernelGGL((compile_kv_kernel<CPL, kFusedRows, kFusedLoadsFirst>), dim3(p.num_token_tiles + 1, num_layers),
+                       dim3(kCompileThreads), compile_lds_bytes(p.num_reqs, TT), s, p, kv);
+}
+
+hipError_t launch_compile_kv(const CompileParams& p, const KVParams& kv, int num_layers, hipStream_t s) {
+    if (num_layers < 1 || !fused_kv_supported(kv.row_bytes)) return hipErrorInvalidValue;
+    if (kv.row_bytes == 1024) launch_fused<1>(p, kv, num_layers, s);
+    else if (kv.row_bytes == 2048) launch_fused<2>(p, kv, num_layers, s);
+    else launch_fused<4>(p, kv, num_layers, s);
     return hipGetLastError();
 }
 

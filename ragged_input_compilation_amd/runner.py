@@ -211,6 +211,15 @@ def reshape_and_cache(kv: KVSet, slot_mapping: int, num_tokens: int, dev_status:
                               stream=current_stream() if stream is None else stream)
 
 
+def compile_and_cache(batch: "Batch", n_pad: int, kv: KVSet, dev_status: int = 0) -> ric.ric_step:
+    """Compile plus the K/V write of every layer in one library call (one
+    kernel for 1/2/4 KiB rows)."""
+    return ric.ric_compile_and_cache(batch.h, n_pad, [t.data_ptr() for t in kv.k], [t.data_ptr() for t in kv.v],
+                                     [t.data_ptr() for t in kv.kc], [t.data_ptr() for t in kv.vc], kv.row_bytes,
+                                     kv.num_slots, src_row_stride=kv.k[0].stride(0) * kv.k[0].element_size(),
+                                     dev_status=dev_status)
+
+
 def gather(hidden: torch.Tensor, idx_ptr: int, dev_count_ptr: int, max_rows: int, out: torch.Tensor,
            dev_status: int = 0, stream: Optional[int] = None) -> None:
     row_bytes = hidden.shape[1] * hidden.element_size()

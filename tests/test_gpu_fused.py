@@ -1,0 +1,174 @@
+"""ric_compile_and_cache (the compile and the K/V write of up to 32 layers in
+one kernel for 1, 2 and 4 KiB rows) against the CPU oracle: every compile
+output bit-exact, every byte of every cache (real rows at the oracle's slots,
+the sentinel everywhere else outside the null block), on the full-size
+configurations, on random batches across block sizes, row sizes and padded
+sizes, past 32 layers, and on rows the fused kernel does not take."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import vectorised
+from tests.gpu_helpers import assert_step_equal, check_cache_exact, expected_step, replay_history
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def rt():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from ragged_input_compilation_amd import _ric, runner
+    return _ric, runner
+
+
+def _prepare(rt, w):
+    ric, runner = rt
+    b = runner.Batch(runner.config_of(w))
+    b.load_history(w)
+    ref, order = replay_history(w)
+    assert b.row_order() == order
+    b.schedule_from(w, order)
+    exp = expected_step(w, ref, use_python=(w.name == "worked_example"))
+    return b, exp
+
+
+def _fused_step(rt, w, b, exp, sentinel, host_sources=False, layers=None):
+    ric, runner = rt
+    L = w.num_layers if layers is None else layers
+    kc, vc = runner.alloc_caches(w, L, fill=sentinel)
+    k, v = runner.alloc_sources(w, exp["n_pad"], seed=w.seed + 29, num_layers=L, host=host_sources)
+    kv = runner.KVSet(k, v, kc, vc, w.row_bytes, w.num_kv_blocks * w.block_size)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    s = runner.compile_and_cache(b, exp["n_pad"], kv, dev_status=status.data_ptr())
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert (s.num_reqs, s.num_actual_tokens, s.num_tokens_padded) == (exp["num_reqs"], exp["num_actual_tokens"],
+                                                                      exp["n_pad"])
+    return s, kv
+
+
+def _check_all(w, exp, kv, sentinel, label):
+    B = w.block_size
+    nslots = w.num_kv_blocks * B
+    null = (w.null_block * B, w.null_block * B + B)
+    for l in range(len(kv.k)):
+        for nm, src, cache in (("K", kv.k[l], kv.kc[l]), ("V", kv.v[l], kv.vc[l])):
+            check_cache_exact(cache, src, exp["slot_mapping"], exp["num_actual_tokens"], sentinel, nslots, null,
+                              f"{label} layer {l} {nm}")
+
+
+@pytest.mark.parametrize("name", ["worked_example", "decode_heavy", "mixed", "churn", "long_context",
+                                  "long_context_forced"])
+def test_fused_step_matches_oracle(rt, name):
+    w = workloads.get(name)
+    b, exp = _prepare(rt, w)
+    sentinel = 0x2C3D
+    s, kv = _fused_step(rt, w, b, exp, sentinel)
+    assert_step_equal(b.step_outputs(s), exp, name)
+    _check_all(w, exp, kv, sentinel, name)
+    del kv
+    torch.cuda.empty_cache()
+    b.close()
+
+
+def _random_workload(rng, trial, head_choices):
+    B = int(rng.choice([1, 2, 3, 4, 8, 16, 32, 64]))
+    R = int(rng.integers(1, 300))
+    max_q = int(rng.choice([1, 5, 40, 300]))
+    M = 2048
+    pool = R * -(-(1200 + max_q) // B) + 10
+    reqs = workloads.random_batch(rng, num_reqs=R, block_size=B, max_model_len=M, num_kv_blocks=pool,
+                                  max_q=max_q, max_c=1200)
+    N = sum(r.num_scheduled for r in reqs)
+    n_pad = N + int(rng.integers(0, 70))
+    heads, dim = head_choices[trial % len(head_choices)]
+    return workloads.Workload("fused_random", block_size=B, max_num_reqs=R + int(rng.integers(0, 20)),
+                              max_model_len=M, max_blocks_per_req=-(-M // B), max_num_batched_tokens=n_pad,
+                              num_kv_blocks=pool, kv_heads=heads, head_dim=dim, kv_dtype="bf16",
+                              num_layers=int(rng.integers(1, 4)), hidden_size=64, gather="all", initial=reqs,
+                              capture_sizes=[n_pad], seed=int(rng.integers(1 << 30)))
+
+
+def test_fused_random_batches(rt):
+    """Sixty seeded batches: block sizes 1 to 64 (shift and division paths),
+    decode-only to 300-token chunks, up to 300 requests, padded tails of up to
+    69 tokens, 1-3 layers, rows of 1, 2 and 4 KiB (fused) and 256 B and 3 KiB
+    (compile, then the separate K/V kernel)."""
+    rng = np.random.default_rng(4321)
+    heads = [(4, 128), (8, 128), (16, 128), (1, 128), (12, 128)]
+    for trial in range(60):
+        w = _random_workload(rng, trial, heads)
+        label = f"trial {trial}: B={w.block_size} R={len(w.initial)} row={w.row_bytes} L={w.num_layers}"
+        b, exp = _prepare(rt, w)
+        sentinel = 0x1357
+        s, kv = _fused_step(rt, w, b, exp, sentinel)
+        assert_step_equal(b.step_outputs(s), exp, label)
+        _check_all(w, exp, kv, sentinel, label)
+        b.close()
+
+
+def test_fused_past_one_launch_of_layers(rt):
+    """40 layers of 2 KiB rows: the fused launch writes the first 32, the K/V
+    kernel the rest; every cache byte is checked."""
+    rng = np.random.default_rng(99)
+    reqs = workloads.random_batch(rng, num_reqs=7, block_size=16, max_model_len=512, num_kv_blocks=300,
+                                  max_q=80, max_c=300)
+    N = sum(r.num_scheduled for r in reqs)
+    w = workloads.Workload("fused_layers", block_size=16, max_num_reqs=8, max_model_len=512,
+                           max_blocks_per_req=32, max_num_batched_tokens=N + 5, num_kv_blocks=300, kv_heads=8,
+                           head_dim=128, kv_dtype="bf16", num_layers=40, hidden_size=64, gather="all",
+                           initial=reqs, capture_sizes=[N + 5], seed=7)
+    b, exp = _prepare(rt, w)
+    s, kv = _fused_step(rt, w, b, exp, 0x0F0F)
+    assert_step_equal(b.step_outputs(s), exp, "40 layers")
+    _check_all(w, exp, kv, 0x0F0F, "40 layers")
+    b.close()
+
+
+def test_fused_equals_separate_calls(rt):
+    """The fused call and ric_compile + ric_reshape_and_cache leave identical
+    caches, null block included when every pad row carries the same bytes."""
+    ric, runner = rt
+    w = workloads.get("mixed")
+    caches = []
+    for fused in (True, False):
+        b, exp = _prepare(rt, w)
+        n_pad = exp["n_pad"]
+        kc, vc = runner.alloc_caches(w, fill=0x4444)
+        k, v = runner.alloc_sources(w, n_pad, seed=w.seed + 3)
+        kv = runner.KVSet(k, v, kc, vc, w.row_bytes, w.num_kv_blocks * w.block_size)
+        if fused:
+            runner.compile_and_cache(b, n_pad, kv)
+        else:
+            s = b.compile(n_pad)
+            runner.reshape_and_cache(kv, s.slot_mapping, n_pad)
+        torch.cuda.synchronize()
+        caches.append((kc[0], vc[0]))
+        b.close()
+    assert torch.equal(caches[0][0], caches[1][0]) and torch.equal(caches[0][1], caches[1][1])
+
+
+def test_fused_argument_errors_enqueue_nothing(rt):
+    ric, runner = rt
+    w = workloads.get("worked_example")
+    b, exp = _prepare(rt, w)
+    kc, vc = runner.alloc_caches(w, fill=0)
+    k, v = runner.alloc_sources(w, exp["n_pad"], seed=1)
+    ptrs = [[t.data_ptr() for t in lst] for lst in (k, v, kc, vc)]
+    nslots = w.num_kv_blocks * w.block_size
+    for kw, code in ((dict(row_bytes=24, num_slots=nslots), ric.RIC_EINVAL),
+                     (dict(row_bytes=w.row_bytes, num_slots=0), ric.RIC_EINVAL),
+                     (dict(row_bytes=w.row_bytes, num_slots=nslots, flags=4), ric.RIC_EINVAL),
+                     (dict(row_bytes=w.row_bytes, num_slots=nslots, src_row_stride=8), ric.RIC_EINVAL)):
+        with pytest.raises(ric.RicError) as e:
+            ric.ric_compile_and_cache(b.h, exp["n_pad"], *ptrs, **kw)
+        assert e.value.code == code
+    with pytest.raises(ric.RicError) as e:
+        ric.ric_compile_and_cache(b.h, exp["n_pad"] + 1000, *ptrs, row_bytes=w.row_bytes, num_slots=nslots)
+    assert e.value.code == ric.RIC_EINVAL
+    s = ric.ric_compile_and_cache(b.h, exp["n_pad"], *ptrs, row_bytes=w.row_bytes, num_slots=nslots)
+    torch.cuda.synchronize()
+    assert_step_equal(b.step_outputs(s), exp, "after rejected calls")
+    b.close()
