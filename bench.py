@@ -2,16 +2,19 @@
 """Benchmark of the ragged-input step on one MI355X.
 
 One step = compile the persistent batch into the flat token stream and its
-metadata (one kernel), write the step's K/V rows into the paged caches of every
-layer (one kernel), gather the hidden rows that produce logits (one kernel).
-Inputs (column store, K/V sources, hidden states) are resident in HBM before
-the timed region.  Steps rotate over independently seeded instances of the
-same configuration (different block tables, token histories and K/V sources),
-so a step never finds the previous steps' bytes in the 256 MB Infinity Cache.
+metadata and write the step's K/V rows into the paged caches of every layer
+(one library call, ric_compile_and_cache: a single kernel, or the compile and
+the K/V kernel when the step is mostly long chunks), then gather the hidden
+rows that produce logits.  Inputs (column store, K/V sources, hidden states)
+are resident in HBM before the timed region.  Steps rotate over independently
+seeded instances of the same configuration (different block tables, token
+histories and K/V sources), so a step never finds the previous steps' bytes in
+the 256 MB Infinity Cache.
 
-Prints one JSON line.  Extra fields: per-kernel times from HIP events, the
-step's algorithmic bytes and GB/s, the rate including the host-to-device
-upload of the step's counts, and the CPU oracle's rate (single thread)."""
+Prints one JSON line: the headline configuration's tokens/s and roofline,
+compile + K/V times of both library paths, the other configurations measured
+the same way (``configs``), and the CPU oracle's rate on one core and on all
+cores."""
 import argparse
 import ctypes
 import hashlib
@@ -21,13 +24,16 @@ import mmap
 import os
 import re
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-KV_EVENT_EVERY = 8      # timed steps carrying events around the K/V launch: 1 in 8 (each pair perturbs its step)
+EVENT_EVERY = 8         # roofline pass: events around the dominant kernel of 1 step in 8
+MIN_EVENT_SAMPLES = 24  # at least this many bracketed launches, whatever --steps is
+FUSE_ALWAYS, FUSE_NEVER = 1, 2
 METRIC = "scheduled tokens/sec per step (compile + KV write); achieved HBM GB/s vs peak"
 DESCRIPTIONS = {
     "worked_example": "3 requests (prefill 7, decode 5+1, chunk 10..21), N=20 padded to 32, block 16, "
@@ -41,6 +47,7 @@ DESCRIPTIONS = {
                     "block 64, bf16 K/V 8x128, 1 layer, compacted hidden gather",
     "long_context_forced": "long_context with request 0 at its last chunk (one compacted gather row)",
 }
+EXTRA_CONFIGS = ["worked_example", "decode_heavy", "mixed", "churn", "long_context"]
 
 
 def parse():
@@ -50,8 +57,12 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="long_context", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--sets", type=int, default=0, help="rotation instances (0: enough for >= 1 GiB/cycle)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-oracle samples")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra-configs", action="store_true",
+                    help="measure only --config (default: also the other configurations, in `configs`)")
+    ap.add_argument("--no-diagnostics", action="store_true",
+                    help="skip the copy ceiling, cached-sources, next-row and cold-cache figures")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB copy (identity-index row gather) for counter scaling")
     return ap.parse_args()
@@ -77,12 +88,26 @@ def step_bytes(w):
 
 
 def kv_kernel_name(w, n_tokens):
-    """Which K/V launch shape the library picks (mirrors its launcher: wave
-    rows for <= 8192 tokens of 1/2/4 KiB rows, otherwise chunk tiles)."""
+    """Which K/V launch shape the library picks for the separate K/V kernel
+    (mirrors its launcher: wave rows for <= 8192 tokens of 1/2/4 KiB rows,
+    otherwise chunk tiles)."""
     cpl = w.row_bytes // 1024
     if w.row_bytes % 1024 == 0 and cpl in (1, 2, 4) and n_tokens <= 8192:
         return "kv_wave_kernel"
     return "kv_chunk_kernel"
+
+
+def fused_path(w):
+    """Whether ric_compile_and_cache takes the single kernel for this step
+    (mirrors the library's rule: 1, 2 or 4 KiB rows, and fewer than 1024
+    scheduled tokens per request on average)."""
+    live = w.live_requests()
+    N = sum(r.num_scheduled for r in live)
+    return w.row_bytes in (1024, 2048, 4096) and N < 1024 * max(len(live), 1)
+
+
+def dominant_kernel(w, n_pad):
+    return "compile_kv_kernel" if fused_path(w) else kv_kernel_name(w, n_pad)
 
 
 def code_digest(text):
@@ -93,32 +118,46 @@ def code_digest(text):
     return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()
 
 
-def kernel_source_digest(text=None):
-    """Digest of the K/V write's code: its load/store helpers, both kernels and
-    their launcher (the source from the load helper up to the row-gather
-    kernel), so that changes elsewhere in the file keep its counters valid.
+# Source regions whose code a kernel's counters depend on: the K/V kernels
+# (load/store helpers, both shapes, their launcher); the compile kernel (its
+# scan, per-token and per-request parts); the single compile + K/V kernel
+# (all of the above and its own code).
+DIGEST_REGIONS = {
+    "kv": ("u32x4 load16(", "// Compile and K/V write in one launch."),
+    "compile": ("int wave_inclusive_scan(", "hipError_t launch_compile("),
+    "compile_kv": ("int wave_inclusive_scan(", "gather_kernel("),
+}
+KERNEL_REGION = {"kv_chunk_kernel": "kv", "kv_wave_kernel": "kv", "compile_kernel": "compile",
+                 "compile_kv_kernel": "compile_kv"}
+
+
+def kernel_source_digest(text=None, region="kv"):
+    """Digest of one region of the kernel source (DIGEST_REGIONS), so that
+    changes elsewhere in the file keep that kernel's counters valid.
     ``text``: the kernel source (default: the file in the package)."""
     if text is None:
         with open(os.path.join(ROOT, "ragged_input_compilation_amd", "csrc", "ric_kernels.hip"),
                   encoding="utf-8") as f:
             text = f.read()
-    start, end = text.find("u32x4 load16("), text.find("gather_kernel(")
+    a, b = DIGEST_REGIONS[region]
+    start, end = text.find(a), text.find(b)
     if start < 0 or end <= start:
-        raise ValueError("the K/V write's code is not where the digest expects it")
+        raise ValueError(f"the {region} code is not where the digest expects it")
     return code_digest(text[start:end])
 
 
 def load_traffic(kernel_name, workload_name):
-    """HBM bytes per launch of the K/V kernel from the committed counter runs
+    """HBM bytes per launch of a kernel from the committed counter runs
     (profiles/<kernel>_<workload>_pmc.md), or None when there are none or they
-    were taken on another version of the kernel source."""
+    were taken on another version of the kernel's source."""
     path = os.path.join(ROOT, "profiles", f"{kernel_name}_{workload_name}_pmc.md")
     if not os.path.exists(path):
         return None
     text = open(path, encoding="utf-8").read()
     digest = re.search(r"^kernel_code_sha256: ([0-9a-f]{64})$", text, re.M)
     traffic = re.search(r"^traffic_bytes_per_launch: (\d+)$", text, re.M)
-    if not digest or not traffic or digest.group(1) != kernel_source_digest():
+    region = KERNEL_REGION.get(kernel_name, "kv")
+    if not digest or not traffic or digest.group(1) != kernel_source_digest(region=region):
         return None
     return int(traffic.group(1))
 
@@ -213,6 +252,9 @@ class GpuStep:
         self.h = ctypes.c_void_p(self.batch.h)
         self.step_out = ric.ric_step()
         self.ric = ric
+        # ric_compile_and_cache with the same K/V arguments (flags last but one)
+        self.ck_args = [self.h, self.n_pad] + self.kv_args[:5] + [
+            0, w.row_bytes, w.num_kv_blocks * w.block_size, None, 0, ctypes.byref(self.step_out)]
 
     def _check(self, rc):
         if rc != 0:
@@ -248,8 +290,19 @@ class GpuStep:
     def compile(self):
         self._check(self.lib.ric_compile(self.h, self.n_pad, ctypes.byref(self.step_out)))
 
+    def compile_kv(self, flags=0):
+        """Compile + K/V write of every layer in one library call; flags 0 is
+        the library's own choice of path."""
+        self.ck_args[-2] = flags
+        self._check(self.lib.ric_compile_and_cache(*self.ck_args))
+
     def kv(self):
         self._check(self.lib.ric_reshape_and_cache(*self.kv_args))
+
+    def whole_step(self):
+        """One whole step: compile + K/V (the library's path), gather."""
+        self.compile_kv()
+        self.gather()
 
     def gather(self):
         self._check(self.lib.ric_gather_rows(*self.gather_args))
@@ -266,92 +319,245 @@ class GpuStep:
         self._check(self.lib.ric_schedule(self.h, ca.shape[0], cp, qp))
 
 
-def cpu_baseline(w, seconds):
-    """The plain C oracle, single thread: compile + K/V scatter into mmap'd host
-    caches of the full size + gather, repeated over the full step."""
-    import numpy as np
-    from oracle import batch as ref_batch, cbind
-    from workloads import payload_numpy
+class _CpuStep:
+    """The step on the host with the plain C oracle: the compile (nano-vllm
+    block-range formulation), a memcpy K/V scatter into mmap'd host caches of
+    the full size (touched pages pre-faulted) and the hidden-row gather."""
 
-    ref = ref_batch.RefBatch(w.max_num_reqs, w.max_model_len, w.max_blocks_per_req, w.num_kv_blocks)
-    for r in w.initial:
-        ref.add_request(r.req_id, r.tokens, r.num_prompt, r.num_computed, r.blocks)
-    for rid in w.finished:
-        ref.remove_request(rid)
-    ref.condense()
-    for r in w.refill:
-        ref.add_request(r.req_id, r.tokens, r.num_prompt, r.num_computed, r.blocks)
-    by_id = w.by_id()
-    order = [rid for rid in ref.req_ids_by_row() if rid is not None]
-    ref.schedule([by_id[i].num_computed for i in order], [by_id[i].num_scheduled for i in order])
-    rows = ref.step_rows()
-    N = sum(r.num_scheduled for r in rows)
-    n_pad = N
-    for s in sorted(w.capture_sizes):
-        if s >= N:
-            n_pad = s
-            break
-    tok, blk = cbind.pack_tables(rows)
-    lib = cbind.lib()
-    i32p = ctypes.POINTER(ctypes.c_int32)
-    c = np.ascontiguousarray([r.num_computed for r in rows], np.int32)
-    q = np.ascontiguousarray([r.num_scheduled for r in rows], np.int32)
-    P = np.ascontiguousarray([r.num_prompt for r in rows], np.int32)
-    MR = w.max_num_reqs
-    outs = {k: np.zeros(n_pad, np.int32) for k in ("ids", "pos", "req", "slot")}
-    per = {k: np.zeros(MR + 1, np.int32) for k in ("qsl", "cuk", "seq", "log", "smp")}
-    disc = np.zeros(MR, np.uint8)
-    p = lambda a: a.ctypes.data_as(i32p)
-    ins = cbind._In(len(rows), w.block_size, MR, n_pad, 0, tok.shape[1], blk.shape[1], p(c), p(q), p(P),
-                    p(tok), p(blk))
-    out = cbind._Out(p(outs["ids"]), p(outs["pos"]), p(outs["req"]), p(outs["slot"]), p(per["qsl"]),
-                     p(per["cuk"]), p(per["seq"]), p(per["log"]), disc.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
-                     p(per["smp"]), 0, 0, 0, 0)
-    rng = np.random.default_rng(w.seed + 99)
-    L = w.num_layers
-    row = w.row_bytes
-    k_src = [payload_numpy(rng, (n_pad, row // 2), w.kv_dtype) for _ in range(L)]
-    v_src = [payload_numpy(rng, (n_pad, row // 2), w.kv_dtype) for _ in range(L)]
-    nslots = w.num_kv_blocks * w.block_size
-    flags = mmap.MAP_PRIVATE | mmap.MAP_ANONYMOUS | getattr(mmap, "MAP_NORESERVE", 0x4000)
-    maps = [mmap.mmap(-1, nslots * row, flags=flags) for _ in range(2 * L)]
-    caches = [np.frombuffer(m, dtype=np.uint8) for m in maps]
-    hidden = np.zeros((n_pad, w.hidden_size * 2), np.uint8)     # lazily mapped zero pages
-    m_rows = MR
-    gout = np.zeros((m_rows, w.hidden_size * 2), np.uint8)
+    def __init__(self, w):
+        import numpy as np
+        from oracle import batch as ref_batch, cbind
+        from workloads import payload_numpy
 
-    def one_step():
-        if lib.nano_compile(ctypes.byref(ins), ctypes.byref(out)) != 0:
+        ref = ref_batch.RefBatch(w.max_num_reqs, w.max_model_len, w.max_blocks_per_req, w.num_kv_blocks)
+        for r in w.initial:
+            ref.add_request(r.req_id, r.tokens, r.num_prompt, r.num_computed, r.blocks)
+        for rid in w.finished:
+            ref.remove_request(rid)
+        ref.condense()
+        for r in w.refill:
+            ref.add_request(r.req_id, r.tokens, r.num_prompt, r.num_computed, r.blocks)
+        by_id = w.by_id()
+        order = [rid for rid in ref.req_ids_by_row() if rid is not None]
+        ref.schedule([by_id[i].num_computed for i in order], [by_id[i].num_scheduled for i in order])
+        rows = ref.step_rows()
+        self.np, self.cbind, self.w = np, cbind, w
+        self.R = len(rows)
+        self.N = sum(r.num_scheduled for r in rows)
+        self.n_pad = self.N
+        for sz in sorted(w.capture_sizes):
+            if sz >= self.N:
+                self.n_pad = sz
+                break
+        self.tok, self.blk = cbind.pack_tables(rows)
+        self.lib = cbind.lib()
+        self.c = np.ascontiguousarray([r.num_computed for r in rows], np.int32)
+        self.q = np.ascontiguousarray([r.num_scheduled for r in rows], np.int32)
+        self.P = np.ascontiguousarray([r.num_prompt for r in rows], np.int32)
+        MR = w.max_num_reqs
+        self.outs = {k: np.zeros(self.n_pad, np.int32) for k in ("ids", "pos", "req", "slot")}
+        self.per = {k: np.zeros(MR + 1, np.int32) for k in ("qsl", "cuk", "seq", "log", "smp")}
+        self.disc = np.zeros(MR, np.uint8)
+        rng = np.random.default_rng(w.seed + 99)
+        self.row = w.row_bytes
+        self.k_src = [payload_numpy(rng, (self.n_pad, self.row // 2), w.kv_dtype) for _ in range(w.num_layers)]
+        self.v_src = [payload_numpy(rng, (self.n_pad, self.row // 2), w.kv_dtype) for _ in range(w.num_layers)]
+        nslots = w.num_kv_blocks * w.block_size
+        flags = mmap.MAP_PRIVATE | mmap.MAP_ANONYMOUS | getattr(mmap, "MAP_NORESERVE", 0x4000)
+        self.maps = [mmap.mmap(-1, nslots * self.row, flags=flags) for _ in range(2 * w.num_layers)]
+        self.caches = [np.frombuffer(m, dtype=np.uint8) for m in self.maps]
+        self.hidden = np.zeros((self.n_pad, w.hidden_size * 2), np.uint8)     # lazily mapped zero pages
+        self.gout = np.zeros((MR, w.hidden_size * 2), np.uint8)
+        self.i32p = ctypes.POINTER(ctypes.c_int32)
+        p = self.p
+        self.ins = cbind._In(self.R, w.block_size, MR, self.n_pad, 0, self.tok.shape[1], self.blk.shape[1],
+                             p(self.c), p(self.q), p(self.P), p(self.tok), p(self.blk))
+        self.out = cbind._Out(p(self.outs["ids"]), p(self.outs["pos"]), p(self.outs["req"]), p(self.outs["slot"]),
+                              p(self.per["qsl"]), p(self.per["cuk"]), p(self.per["seq"]), p(self.per["log"]),
+                              self.disc.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), p(self.per["smp"]),
+                              0, 0, 0, 0)
+
+    def p(self, a, off=0):
+        return ctypes.cast(a.ctypes.data + 4 * off, self.i32p)
+
+    def close(self):
+        self.caches = None
+        for m in self.maps:
+            m.close()
+
+    def gather(self):
+        w = self.w
+        idx = self.per["log"] if w.gather == "all" else self.per["smp"]
+        cnt = self.R if w.gather == "all" else self.out.num_sampled
+        self.lib.nano_gather(self.hidden.ctypes.data, self.hidden.shape[1], self.p(idx), cnt, self.gout.ctypes.data)
+
+    def scatter(self, t0, t1):
+        row = self.row
+        for l in range(self.w.num_layers):
+            self.lib.nano_kv_scatter(self.k_src[l].ctypes.data + t0 * row, self.v_src[l].ctypes.data + t0 * row,
+                                     self.caches[2 * l].ctypes.data, self.caches[2 * l + 1].ctypes.data,
+                                     self.p(self.outs["slot"], t0), t1 - t0, row)
+
+    def single(self):
+        """The whole step on one thread."""
+        if self.lib.nano_compile(ctypes.byref(self.ins), ctypes.byref(self.out)) != 0:
             raise RuntimeError("oracle rejected the step")
-        for l in range(L):
-            lib.nano_kv_scatter(k_src[l].ctypes.data, v_src[l].ctypes.data, caches[2 * l].ctypes.data,
-                                caches[2 * l + 1].ctypes.data, p(outs["slot"]), n_pad, row)
-        idx = per["log"] if w.gather == "all" else per["smp"]
-        cnt = len(rows) if w.gather == "all" else out.num_sampled
-        lib.nano_gather(hidden.ctypes.data, hidden.shape[1], p(idx), cnt, gout.ctypes.data)
+        self.scatter(0, self.n_pad)
+        self.gather()
 
-    one_step()                     # pre-fault the touched cache pages
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        one_step()
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or reps >= 10000:
-            break
-    del caches
-    for m in maps:
-        m.close()
-    return dict(value=N * reps / el, unit="tokens/s", cores=1, kind="oracle",
-                host_cpu_count=os.cpu_count(), host_cpus_allowed=len(os.sched_getaffinity(0)),
-                sample=f"{reps} full steps of the same configuration (seed instance 0) in {el:.1f} s; "
-                       f"single-thread C oracle (nano-vllm block-range compile, memcpy K/V scatter into "
-                       f"mmap'd full-size host caches, hidden-row gather)")
+
+class _CpuParallel:
+    """The same step split by requests over a pool of threads: thread k
+    compiles one contiguous range of requests (balanced by scheduled tokens)
+    as a batch of its own, shifts its range's request-relative outputs into
+    place, and writes its range's K/V rows; the main thread then fills in the
+    running totals across ranges, the compacted sample list, the padding and
+    the gather.  The C calls release the interpreter lock."""
+
+    def __init__(self, cs, threads):
+        np = cs.np
+        self.cs = cs
+        cu = np.concatenate([[0], np.cumsum(cs.q, dtype=np.int64)])
+        T = max(1, min(threads, cs.R))
+        cuts = [0] + [int(np.searchsorted(cu, cs.N * k / T, side="left")) for k in range(1, T)] + [cs.R]
+        self.ranges = [(a, b, int(cu[a]), int(cu[b])) for a, b in zip(cuts[:-1], cuts[1:]) if b > a]
+        self.locals = []
+        w = cs.w
+        for r0, r1, t0, t1 in self.ranges:
+            n = r1 - r0
+            loc = {k: np.zeros(n + 1, np.int32) for k in ("qsl", "cuk", "log", "smp")}
+            p = cs.p
+            ins = cs.cbind._In(n, w.block_size, n, t1 - t0, 0, cs.tok.shape[1], cs.blk.shape[1], p(cs.c, r0),
+                               p(cs.q, r0), p(cs.P, r0), p(cs.tok, r0 * cs.tok.shape[1]),
+                               p(cs.blk, r0 * cs.blk.shape[1]))
+            out = cs.cbind._Out(p(cs.outs["ids"], t0), p(cs.outs["pos"], t0), p(cs.outs["req"], t0),
+                                p(cs.outs["slot"], t0), p(loc["qsl"]), p(loc["cuk"]), p(cs.per["seq"], r0),
+                                p(loc["log"]),
+                                ctypes.cast(cs.disc.ctypes.data + r0, ctypes.POINTER(ctypes.c_uint8)),
+                                p(loc["smp"]), 0, 0, 0, 0)
+            self.locals.append((loc, ins, out))
+        self.threads_used = len(self.ranges)
+        self.start = threading.Barrier(self.threads_used + 1)
+        self.done = threading.Barrier(self.threads_used + 1)
+        self.stop = False
+        self.workers = [threading.Thread(target=self._work, args=(k,), daemon=True) for k in range(self.threads_used)]
+        for t in self.workers:
+            t.start()
+
+    def _work(self, k):
+        cs = self.cs
+        r0, r1, t0, t1 = self.ranges[k]
+        loc, ins, out = self.locals[k]
+        while True:
+            self.start.wait()
+            if self.stop:
+                return
+            if cs.lib.nano_compile(ctypes.byref(ins), ctypes.byref(out)) != 0:
+                raise RuntimeError("oracle rejected a range")
+            cs.outs["req"][t0:t1] += r0
+            cs.per["qsl"][r0 + 1:r1 + 1] = loc["qsl"][1:] + t0
+            cs.per["log"][r0:r1] = loc["log"][:r1 - r0] + t0
+            cs.scatter(t0, t1)
+            self.done.wait()
+
+    def step(self):
+        cs, np = self.cs, self.cs.np
+        self.start.wait()
+        self.done.wait()
+        R, N, MR = cs.R, cs.N, cs.w.max_num_reqs
+        per = cs.per
+        base = 0
+        for (r0, r1, t0, t1), (loc, _, _) in zip(self.ranges, self.locals):
+            per["cuk"][r0 + 1:r1 + 1] = loc["cuk"][1:r1 - r0 + 1] + base
+            base += int(loc["cuk"][r1 - r0])
+        per["qsl"][0] = per["cuk"][0] = 0
+        per["qsl"][R + 1:] = N
+        per["cuk"][R + 1:] = base
+        per["seq"][R:MR] = 0
+        per["log"][R:MR] = -1
+        cs.disc[R:MR] = 1
+        keep = per["log"][:R][cs.disc[:R] == 0]
+        per["smp"][:keep.shape[0]] = keep
+        per["smp"][keep.shape[0]:MR] = -1
+        cs.out.num_sampled = int(keep.shape[0])
+        o = cs.outs
+        o["ids"][N:] = 0
+        o["pos"][N:] = 0
+        o["req"][N:] = -1
+        o["slot"][N:] = cs.w.null_block * cs.w.block_size
+        if N < cs.n_pad:
+            cs.scatter(N, cs.n_pad)
+        cs.gather()
+
+    def close(self):
+        self.stop = True
+        self.start.wait()
+        for t in self.workers:
+            t.join()
+
+
+def _median_rate(fn, tokens, seconds, blocks=5):
+    """Median over `blocks` timed blocks of the scheduled tokens per second,
+    each block running whole steps for about seconds / blocks."""
+    rates, steps = [], 0
+    for _ in range(blocks):
+        n, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds / blocks or n >= 5000:
+                break
+        rates.append(tokens * n / el)
+        steps += n
+    return sorted(rates)[blocks // 2], steps
+
+
+def cpu_baseline(w, seconds):
+    """The plain C oracle timed on this host: one thread, then the per-request
+    parallel split on every core this process may use.  Each is the median of
+    5 timed blocks of whole steps; the parallel step's outputs are checked
+    against the single-thread step's before timing."""
+    cs = _CpuStep(w)
+    cs.single()                    # pre-fault the touched cache pages
+    want = {k: v.copy() for k, v in cs.outs.items()}
+    want.update({k: v.copy() for k, v in cs.per.items()})
+    want_disc = cs.disc.copy()
+    allowed = len(os.sched_getaffinity(0))
+    one, n1 = _median_rate(cs.single, cs.N, seconds / 2)
+    par = _CpuParallel(cs, allowed)
+    for d in list(cs.outs.values()) + list(cs.per.values()):
+        d.fill(-9)
+    par.step()
+    got = dict(cs.outs, **cs.per)
+    R, MR = cs.R, w.max_num_reqs
+    for k in ("ids", "pos", "req", "slot"):
+        assert (got[k] == want[k]).all(), f"parallel CPU step differs in {k}"
+    for k in ("qsl", "cuk"):
+        assert (got[k][:MR + 1] == want[k][:MR + 1]).all(), f"parallel CPU step differs in {k}"
+    for k in ("seq", "log", "smp"):
+        assert (got[k][:MR] == want[k][:MR]).all(), f"parallel CPU step differs in {k}"
+    assert (cs.disc == want_disc).all()
+    many, n2 = _median_rate(par.step, cs.N, seconds / 2)
+    par.close()
+    cs.close()
+    return dict(value=one, unit="tokens/s", cores=1, kind="oracle", host_cpu_count=os.cpu_count(),
+                host_cpus_allowed=allowed,
+                sample=f"median of 5 blocks of whole steps of the same configuration (seed instance 0), "
+                       f"{n1} steps in {seconds / 2:.0f} s; single-thread C oracle (nano-vllm block-range "
+                       f"compile, memcpy K/V scatter into mmap'd full-size host caches, hidden-row gather)",
+                all_cores=dict(value=many, unit="tokens/s", cores=par.threads_used, pool=allowed,
+                               sample=f"median of 5 blocks, {n2} steps in {seconds / 2:.0f} s; the same oracle "
+                                      f"on {par.threads_used} threads, one contiguous range of requests each "
+                                      f"(balanced by scheduled tokens; per-request parallelism, so never more "
+                                      f"threads than requests), K/V rows split the same way"))
 
 
 def kv_sources_cached(ric, torch, sets, nbytes, reps=20):
-    """The K/V launch right after its sources were rewritten in place (x * 1
-    by a torch kernel), so that they sit in the caches as they do when the
-    write follows the K/V projection inside a model."""
+    """Compile + K/V (the library's path) right after the K/V sources were
+    rewritten in place (x * 1 by a torch kernel), so that they sit in the
+    caches as they do when the write follows the K/V projection inside a
+    model."""
     times = []
     for i in range(reps + 2):
         st = sets[i % len(sets)]
@@ -359,7 +565,7 @@ def kv_sources_cached(ric, torch, sets, nbytes, reps=20):
             t.mul_(1)
         a, b = Event(), Event()
         a.record()
-        st.kv()
+        st.compile_kv()
         b.record()
         times.append((a, b))
     torch.cuda.synchronize()
@@ -541,6 +747,108 @@ def calibrate_copy(ric, torch, stream):
                 gbps=2 * rows * row / (ms * 1e-3) / 1e9, grid=rows)
 
 
+def build_sets(ric, runner, torch, workloads, name, nsets=0):
+    """Rotation instances of one configuration (enough that a cycle moves
+    >= 1 GiB unless `nsets` is given), sharing one set of caches, hidden rows
+    and gather output."""
+    w0 = workloads.get(name)
+    sb = step_bytes(w0)
+    S = nsets or max(2, min(16, math.ceil((1 << 30) / sb["total"])))
+    kc, vc = runner.alloc_caches(w0)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(w0.seed + 5)
+    n_pad0 = ric.ric_padded_size(w0.capture_sizes, sb["N"])
+    hidden = torch.randn((n_pad0, w0.hidden_size), generator=g, device="cuda").to(torch.bfloat16)
+    gout = torch.empty((w0.max_num_reqs, w0.hidden_size), dtype=torch.bfloat16, device="cuda")
+    sets = []
+    for k in range(S):
+        w = w0 if k == 0 else workloads.get(name, variant=k)
+        sets.append(GpuStep(ric, runner, torch, w, kc, vc, hidden, gout, seed=w.seed + 31))
+        print(f"[bench] {name}: set {k + 1}/{S} ready", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    return w0, sb, sets
+
+
+def release(torch, sets):
+    for st in sets:
+        st.batch.close()
+    sets.clear()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def timed_steps(torch, sets, steps, warmup):
+    """Wall-clock ms per step of `steps` whole steps after `warmup` untimed
+    ones, bracketed by device synchronisation on both sides."""
+    for i in range(warmup):
+        sets[i % len(sets)].whole_step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        sets[i % len(sets)].whole_step()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def bracketed(torch, sets, before, body, after, reps, flush_buf=None):
+    """Median ms of `body(st)` between two events over `reps` rotating steps;
+    `before` / `after` run outside the events (the rest of the step), and a
+    1 GiB read evicts the caches before each rep when flush_buf is given."""
+    pairs = [(Event(), Event()) for _ in range(reps)]
+    for i in range(reps):
+        st = sets[i % len(sets)]
+        if flush_buf is not None:
+            flush_buf.sum()
+        before(st)
+        a, b = pairs[i]
+        a.record()
+        body(st)
+        b.record()
+        after(st)
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) for a, b in pairs)[reps // 2]
+
+
+def compile_kv_paths(torch, sets, sb, reps, cold_reps, flush_buf):
+    """Compile + K/V write of every layer through ric_compile_and_cache, for
+    the library's own choice of path and for each path forced: events around
+    the call (warm: back to back, rotating instances; after flush: a 1 GiB
+    read first), gather outside."""
+    nbytes = sb["compile"] + sb["kv"]
+    out = {"bytes": nbytes}
+    nothing = lambda st: None
+    for name, flags in (("auto", 0), ("single_kernel", FUSE_ALWAYS), ("two_kernels", FUSE_NEVER)):
+        for st in sets:
+            st.compile_kv(flags)
+        body = lambda st, f=flags: st.compile_kv(f)
+        gather = lambda st: st.gather()
+        warm = bracketed(torch, sets, nothing, body, gather, reps)
+        cold = bracketed(torch, sets, nothing, body, gather, cold_reps, flush_buf)
+        out[name] = {"warm_us": warm * 1e3, "warm_frac_of_peak": nbytes / (warm * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                     "after_cache_flush_us": cold * 1e3,
+                     "after_cache_flush_frac_of_peak": nbytes / (cold * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+    return out
+
+
+def extra_config(ric, runner, torch, workloads, name, steps, warmup):
+    """Another configuration measured the same way as the headline (fewer
+    diagnostics): whole-step tokens/s, and compile + K/V by both paths."""
+    t0 = time.perf_counter()
+    w0, sb, sets = build_sets(ric, runner, torch, workloads, name)
+    ms = timed_steps(torch, sets, steps, warmup)
+    flush_buf = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+    ck = compile_kv_paths(torch, sets, sb, 30, 10, flush_buf)
+    del flush_buf
+    path = "single_kernel" if fused_path(w0) else "two_kernels"
+    res = {"workload": f"{name}: {DESCRIPTIONS[name]}", "num_reqs": sb["R"], "num_tokens": sb["N"],
+           "num_layers": w0.num_layers, "tokens_per_s": sb["N"] / (ms * 1e-3), "ms_per_step": ms,
+           "step_bytes": sb["total"], "library_path": path, "compile_plus_kv": ck,
+           "rotation_instances": len(sets), "seconds": None}
+    release(torch, sets)
+    res["seconds"] = time.perf_counter() - t0
+    return res
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -550,7 +858,6 @@ def main():
               f"parallelism each runs the same compile and writes its own K/V heads, so the per-GPU figure is "
               f"the one to measure.", file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
     import workloads
     from ragged_input_compilation_amd import _ric as ric, runner
@@ -559,137 +866,87 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     Event.stream = runner.current_stream()     # every library call below runs on this stream
-    w0 = workloads.get(args.config)
-    sb = step_bytes(w0)
-    S = args.sets or max(2, min(16, math.ceil((1 << 30) / sb["total"])))
     t_setup = time.perf_counter()
-    kc, vc = runner.alloc_caches(w0)
-    g = torch.Generator(device="cuda")
-    g.manual_seed(w0.seed + 5)
-    n_pad0 = ric.ric_padded_size(w0.capture_sizes, sb["N"])
-    hidden = torch.randn((n_pad0, w0.hidden_size), generator=g, device="cuda").to(torch.bfloat16)
-    gout = torch.empty((w0.max_num_reqs, w0.hidden_size), dtype=torch.bfloat16, device="cuda")
-    sets = []
-    for k in range(S):
-        w = w0 if k == 0 else workloads.get(args.config, variant=k)
-        sets.append(GpuStep(ric, runner, torch, w, kc, vc, hidden, gout, seed=w.seed + 31))
-        print(f"[bench] set {k + 1}/{S} ready", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
+    w0, sb, sets = build_sets(ric, runner, torch, workloads, args.config, args.sets)
+    S = len(sets)
     setup_s = time.perf_counter() - t_setup
+    fused = fused_path(w0)
+    kernel = dominant_kernel(w0, sets[0].n_pad)
 
-    def event_pairs(n):
-        return [(Event(), Event())
-                for _ in range((n + KV_EVENT_EVERY - 1) // KV_EVENT_EVERY)]
+    # The timed region: whole steps, no events.
+    ms_per_step = timed_steps(torch, sets, args.steps, args.warmup)
 
-    def run(n, mode, pool=None):
-        """mode "none": no events; "kv": events around the K/V launch only (the
-        timed region; `pool` holds the events, created beforehand since
-        creating them costs host time); "all": events around each of the three
-        kernels."""
-        ev = []
-        for i in range(n):
-            st = sets[i % S]
-            if mode == "none":
-                st.compile()
-                st.kv()
-                st.gather()
-            elif mode == "kv" and i % KV_EVENT_EVERY != 0:
-                st.compile()
-                st.kv()
-                st.gather()
-            elif mode == "kv":
-                a, b = pool[i // KV_EVENT_EVERY]
-                st.compile()
-                a.record()
-                st.kv()
-                b.record()
-                st.gather()
-                ev.append((a, b))
-            else:
-                e = [Event() for _ in range(6)]
-                e[0].record(); st.compile(); e[1].record()
-                e[2].record(); st.kv(); e[3].record()
-                e[4].record(); st.gather(); e[5].record()
-                ev.append(e)
-        return ev
-
-    run(args.warmup, "none")
-    pool = event_pairs(args.steps)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev = run(args.steps, "kv", pool)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    mean = lambda xs: sum(xs) / len(xs)
-    kv_mean = mean([a.elapsed_time(b) for a, b in ev])
-
-    # Untimed diagnostics: the same steps with no events, then with events
-    # around every kernel (compile and gather durations).
-    torch.cuda.synchronize()
-    t2 = time.perf_counter()
-    run(args.steps, "none")
-    host_ms = (time.perf_counter() - t2) * 1e3 / args.steps     # enqueue only: the launches are asynchronous
-    torch.cuda.synchronize()
-    ms_no_events = (time.perf_counter() - t2) * 1e3 / args.steps
-    evs = run(min(args.steps, 100), "all")
-    torch.cuda.synchronize()
-    comp_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    ga_ms = [e[4].elapsed_time(e[5]) for e in evs]
-
-    # Same step with the counts uploaded from the host first (schedule + the
-    # flush inside compile carry them over PCIe).
-    for st in sets:                      # builds each instance's host count arrays once
-        st.reschedule()
-        st.compile()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    n_pcie = max(args.steps // 2, 1)
-    for i in range(n_pcie):
+    # Roofline pass: the same steps, with events around the dominant kernel
+    # of one step in EVENT_EVERY, at least MIN_EVENT_SAMPLES of them.
+    n_roof = max(args.steps, MIN_EVENT_SAMPLES * EVENT_EVERY)
+    pairs = [(Event(), Event()) for _ in range(-(-n_roof // EVENT_EVERY))]
+    for i in range(n_roof):
         st = sets[i % S]
-        st.reschedule()
-        st.compile()
-        st.kv()
+        if i % EVENT_EVERY:
+            st.whole_step()
+            continue
+        a, b = pairs[i // EVENT_EVERY]
+        if fused:
+            a.record(); st.compile_kv(); b.record()
+        else:
+            st.compile(); a.record(); st.kv(); b.record()
         st.gather()
     torch.cuda.synchronize()
-    pcie_ms = (time.perf_counter() - t1) * 1e3 / n_pcie
+    dom_ms = sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
+    dom_bytes = sb["compile"] + sb["kv"] if fused else sb["kv"]
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
 
-    # Cold caches: before each of 50 reps, a 1 GiB read (a sum) evicts the
-    # Infinity Cache and the L2s without leaving dirty lines behind; events
-    # then bracket compile + K/V (and the K/V launch alone).
     flush_buf = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
-    median = lambda xs: sorted(xs)[len(xs) // 2]
-
-    def bracketed(n, flush, with_compile):
-        pairs = event_pairs(n * KV_EVENT_EVERY)
-        for i in range(n):
-            st = sets[i % S]
-            if flush:
-                flush_buf.sum()
-            elif not with_compile:
-                st.compile()
-            a, b = pairs[i]
-            a.record()
-            if with_compile:
-                st.compile()
-            st.kv()
-            b.record()
-            st.gather()
-        torch.cuda.synchronize()
-        return median([a.elapsed_time(b) for a, b in pairs])
-
-    kv_cold_ms = bracketed(20, True, False)
-    ck_cold_ms = bracketed(50, True, True)
-    ck_warm_ms = bracketed(50, False, True)
+    ck = compile_kv_paths(torch, sets, sb, 50, 30, flush_buf)
+    nothing = lambda st: None
+    comp_ms = bracketed(torch, sets, nothing, lambda st: st.compile(), lambda st: (st.kv(), st.gather()), 50)
+    kv_ms = bracketed(torch, sets, lambda st: st.compile(), lambda st: st.kv(), lambda st: st.gather(), 50)
+    kv_cold_ms = bracketed(torch, sets, lambda st: st.compile(), lambda st: st.kv(), lambda st: st.gather(), 20,
+                           flush_buf)
+    ga_ms = bracketed(torch, sets, lambda st: st.compile_kv(), lambda st: st.gather(), nothing, 50) \
+        if sets[0].gather_rows else None
     del flush_buf
-    ceiling = copy_ceiling(ric, torch, sets, w0, sb)
-    cached = kv_sources_cached(ric, torch, sets, sb["kv"])
-    nxt = next_rows(ric, runner, torch, w0, sets[0])
 
+    diag = {}
+    if not args.no_diagnostics:
+        # host enqueue cost of a step, and the step with its counts uploaded
+        # from the host first (schedule + the flush inside the compile)
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        for i in range(args.steps):
+            sets[i % S].whole_step()
+        diag["host_enqueue_us_per_step"] = (time.perf_counter() - t2) * 1e6 / args.steps
+        torch.cuda.synchronize()
+        for st in sets:
+            st.reschedule()
+            st.compile_kv()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        n_pcie = max(args.steps // 2, 1)
+        for i in range(n_pcie):
+            st = sets[i % S]
+            st.reschedule()
+            st.whole_step()
+        torch.cuda.synchronize()
+        diag["pcie_inclusive_tokens_per_s"] = sb["N"] / ((time.perf_counter() - t1) / n_pcie)
+        diag["copy_ceiling"] = copy_ceiling(ric, torch, sets, w0, sb)
+        diag["kv_sources_cached"] = kv_sources_cached(ric, torch, sets, sb["compile"] + sb["kv"])
+        diag["next_rows"] = next_rows(ric, runner, torch, w0, sets[0])
     calib = calibrate_copy(ric, torch, runner.current_stream()) if args.calibrate_copy else None
+    condense = ({"us_with_host_planning_and_pair_upload": sum(st.condense["us"] for st in sets) / S,
+                 "rows_moved": sets[0].condense["rows_moved"], "bytes": sets[0].condense["bytes"],
+                 "instances": S} if sets[0].condense else None)
+    release(torch, sets)
+
+    configs = {}
+    if not args.no_extra_configs:
+        for name in EXTRA_CONFIGS:
+            if name != args.config:
+                configs[name] = extra_config(ric, runner, torch, workloads, name, max(args.steps, 50),
+                                             max(args.warmup, 10))
 
     N = sb["N"]
-    achieved = sb["kv"] / (kv_mean * 1e-3) / 1e9
+    ceiling = diag.get("copy_ceiling")
     res = {
         "metric": METRIC,
         "value": N / (ms_per_step * 1e-3),
@@ -704,44 +961,29 @@ def main():
         "dtype": "int32",
         "data": "synthetic",
         "config": {"workload": f"{args.config}: {DESCRIPTIONS[args.config]}", "num_reqs": sb["R"],
-                   "num_tokens": N, "num_layers": w0.num_layers, "rotation_instances": S},
+                   "num_tokens": N, "num_layers": w0.num_layers, "rotation_instances": S,
+                   "library_path": "single_kernel" if fused else "two_kernels"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": load_traffic(kv_kernel_name(w0, sets[0].n_pad), args.config),
-                     "kernel": kv_kernel_name(w0, sets[0].n_pad), "kv_flags": sets[0].kv_flags,
-                     "bytes_per_launch": sb["kv"],
-                     "avg_launch_us": kv_mean * 1e3, "event_samples": len(ev),
-                     "frac_of_copy_ceiling": achieved / max(ceiling["torch_copy_gbps"],
-                                                            ceiling["identity_slots_gbps"])},
-        "copy_ceiling": ceiling,
-        "kv_sources_cached": cached,
-        "compile_plus_kv": {"bytes": sb["compile"] + sb["kv"],
-                            "warm_us": ck_warm_ms * 1e3,
-                            "warm_frac_of_peak": (sb["compile"] + sb["kv"]) / (ck_warm_ms * 1e-3) / 1e9
-                            / HBM_PEAK_GBPS,
-                            "after_cache_flush_us": ck_cold_ms * 1e3,
-                            "after_cache_flush_frac_of_peak": (sb["compile"] + sb["kv"]) / (ck_cold_ms * 1e-3)
-                            / 1e9 / HBM_PEAK_GBPS},
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": load_traffic(kernel, args.config),
+                     "kernel": kernel, "bytes_per_launch": dom_bytes, "avg_launch_us": dom_ms * 1e3,
+                     "event_samples": len(pairs),
+                     "frac_of_copy_ceiling": (achieved / max(ceiling["torch_copy_gbps"], ceiling["identity_slots_gbps"])
+                                              if ceiling else None)},
+        "compile_plus_kv": ck,
+        "kernels_us": {"compile": comp_ms * 1e3, "kv_scatter": kv_ms * 1e3,
+                       "kv_scatter_after_cache_flush": kv_cold_ms * 1e3,
+                       "gather": ga_ms * 1e3 if ga_ms is not None else None},
         "step_bytes": sb["total"],
         "step_gbps": sb["total"] / (ms_per_step * 1e-3) / 1e9,
         "step_frac_of_peak": sb["total"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-        "ms_per_step_without_events": ms_no_events,
-        "host_enqueue_us_per_step": host_ms * 1e3,
-        "kernels_us": {"compile": mean(comp_ms) * 1e3, "kv_scatter": kv_mean * 1e3,
-                       "gather": mean(ga_ms) * 1e3 if sets[0].gather_rows else None,
-                       "kv_scatter_after_cache_flush": kv_cold_ms * 1e3},
-        "pcie_inclusive_tokens_per_s": N / (pcie_ms * 1e-3),
-        "next_rows": nxt,
-        "condense": ({"us_with_host_planning_and_pair_upload": mean([st.condense["us"] for st in sets]),
-                      "rows_moved": sets[0].condense["rows_moved"], "bytes": sets[0].condense["bytes"],
-                      "instances": S} if sets[0].condense else None),
+        "condense": condense,
         "setup_s": setup_s,
+        "configs": configs,
     }
+    res.update(diag)
     if calib:
         res["copy_calibration"] = calib
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w0, args.cpu_seconds)
-    else:
-        res["cpu_baseline"] = None
+    res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(w0, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 

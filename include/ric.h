@@ -374,15 +374,21 @@ int ric_compile(ric_batch* b, int32_t num_tokens_padded, ric_step* out);
  * the same outputs and cache contents as those two calls
  * ([P1 §3. 物理 KV 槽位], [P3 §实现]: each token's K/V row goes to the slot the
  * compile gives it).  For rows of 1, 2 or 4 KiB the compile and the K/V write
- * of up to 32 layers are one kernel: each workgroup derives its own tokens'
- * slots and copies their rows, so there is no second launch to wait for;
- * other row sizes and further layers use the separate K/V kernel after the
- * compile.  The K/V arguments are those of ric_reshape_and_cache (k, v,
- * k_cache, v_cache: host arrays of num_layers device pointers; src_row_stride
- * 0 = row_bytes; dev_status optional; flags must be 0).  Padded tokens write
- * their rows into the null block, as ric_reshape_and_cache does with the
- * padded slot mapping.  Errors: those of ric_compile and of
- * ric_reshape_and_cache; on an argument error nothing is enqueued. */
+ * of up to 32 layers can be one kernel: each workgroup derives its own
+ * tokens' slots and copies their rows, so there is no second launch to wait
+ * for.  flags picks the path: 0 lets the library choose (one kernel unless
+ * the scheduled tokens average 1024 or more per request, where the separate
+ * K/V kernel streams long contiguous runs faster), RIC_FUSE_ALWAYS and
+ * RIC_FUSE_NEVER force it; any other bit is EINVAL.  Other row sizes and
+ * layers past 32 use the separate K/V kernel after the compile.  The other
+ * K/V arguments are those of ric_reshape_and_cache (k, v, k_cache, v_cache:
+ * host arrays of num_layers device pointers; src_row_stride 0 = row_bytes;
+ * dev_status optional).  Padded tokens write their rows into the null block,
+ * as ric_reshape_and_cache does with the padded slot mapping.  Errors: those
+ * of ric_compile and of ric_reshape_and_cache; on an argument error nothing
+ * is enqueued. */
+#define RIC_FUSE_ALWAYS 1u
+#define RIC_FUSE_NEVER  2u
 int ric_compile_and_cache(ric_batch* b, int32_t num_tokens_padded, const void* const* k, const void* const* v,
                           void* const* k_cache, void* const* v_cache, int32_t num_layers, int64_t src_row_stride,
                           int32_t row_bytes, int64_t num_slots, int32_t* dev_status, uint32_t flags,

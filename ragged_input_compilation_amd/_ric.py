@@ -33,6 +33,7 @@ class RicError(RuntimeError):
 
 
 RIC_MAX_KV_GROUPS, RIC_SLOTS_PER_TOKEN, RIC_SLOTS_NONE = 4, 0, 1
+RIC_FUSE_ALWAYS, RIC_FUSE_NEVER = 1, 2
 
 
 class ric_config(ctypes.Structure):

@@ -1198,16 +1198,26 @@ int ric_compile_and_cache(ric_batch* b, int32_t n_pad, const void* const* k, con
     DeviceScope ds(b);
     int rc = check_compile_args(b, n_pad);
     if (rc) return rc;
+    const uint32_t path = flags & 3u;
+    if (path == 3u) return fail(RIC_EINVAL, "flags 0x%x: RIC_FUSE_ALWAYS and RIC_FUSE_NEVER together", flags);
     KVParams kv{};
     rc = kv_params(k, v, k_cache, v_cache, num_layers, n_pad, src_row_stride, row_bytes, num_slots, dev_status,
-                   flags, &kv);
+                   flags & ~3u, &kv);
     if (rc) return rc;
     rc = flush(b);
     if (rc) return rc;
     const CompileParams p = compile_params(b, n_pad);
     kv.slot = b->d_slot;
+    // The library's own choice: one kernel unless the step is mostly long
+    // per-request runs (on average 1024 or more tokens per request), where the
+    // K/V kernel's small tiles stream contiguous rows at the copy ceiling and
+    // the fused kernel's wave rows measured up to 15% slower on some machines
+    // (long-context: 52 vs 46 us for the copy alone).
+    bool fuse = path == RIC_FUSE_ALWAYS ||
+                (path == 0 && (int64_t)b->sched_N < (int64_t)1024 * std::max<int32_t>(b->sched_R, 1));
+    fuse = fuse && num_layers > 0 && n_pad > 0 && fused_kv_supported(row_bytes);
     int32_t done = 0;
-    if (num_layers > 0 && n_pad > 0 && fused_kv_supported(row_bytes)) {
+    if (fuse) {
         done = std::min<int32_t>(kMaxLayersPerLaunch, num_layers);
         set_layers(&kv, k, v, k_cache, v_cache, 0, done);
         HIP_TRY(launch_compile_kv(p, kv, done, b->stream));

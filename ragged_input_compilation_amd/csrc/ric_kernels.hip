@@ -504,17 +504,16 @@ hipError_t launch_kv_scatter(const KVParams& p_in, int num_layers, hipStream_t s
 // ---------------------------------------------------------------------------
 // Compile and K/V write in one launch.  blockIdx.y = layer; workgroup x <
 // num_token_tiles owns TT = ROWS * 4 consecutive tokens, the last one (layer 0
-// only) writes the per-request outputs.  Each token workgroup rebuilds
-// query_start_loc in LDS like the compile kernel, derives its tokens' slots
-// (layer-0 workgroups also write the per-token outputs) and copies its
-// tokens' K and V rows of its layer to those slots, wave by wave as the wave
-// kernel does.  This saves the second launch and the drain between the two
-// kernels, and lets the K/V copy of one tile overlap the slot work of
-// another.  With LOADS_FIRST the source rows are loaded before the prefix
-// sum (they do not depend on it).  A slot outside [0, num_slots) skips its
-// row and counts in *status, as in the K/V kernels.
+// only) writes the per-request outputs.  Each token workgroup first issues
+// the loads of its tokens' K and V rows of its layer (they do not depend on
+// the compile), then rebuilds query_start_loc in LDS like the compile kernel,
+// derives its tokens' slots (layer-0 workgroups also write the per-token
+// outputs) and stores the rows, wave by wave as the wave kernel does.  This
+// saves the second launch and the drain between two kernels, and the loads of
+// a tile overlap its slot work.  A slot outside [0, num_slots) skips its row
+// and counts in *status, as in the K/V kernels.
 // ---------------------------------------------------------------------------
-template <int CPL, int ROWS, bool LOADS_FIRST>
+template <int CPL, int ROWS>
 __global__ __launch_bounds__(kCompileThreads) void compile_kv_kernel(CompileParams p, KVParams kv) {
     constexpr int WAVES = kCompileThreads / kWave;
     constexpr int TT = ROWS * WAVES;
@@ -528,10 +527,10 @@ __global__ __launch_bounds__(kCompileThreads) void compile_kv_kernel(CompilePara
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int tile0 = blockIdx.x * TT;
     const int t0 = tile0 + wid * ROWS;         // this wave's first row
-    const uint8_t* __restrict__ ks = kv.k[layer];
-    const uint8_t* __restrict__ vs = kv.v[layer];
     u32x4 a[ROWS][2 * CPL];
-    auto load_rows = [&]() {
+    if (!req_wg) {
+        const uint8_t* __restrict__ ks = kv.k[layer];
+        const uint8_t* __restrict__ vs = kv.v[layer];
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
             const int t = t0 + r;
@@ -544,8 +543,7 @@ __global__ __launch_bounds__(kCompileThreads) void compile_kv_kernel(CompilePara
                 }
             }
         }
-    };
-    if (LOADS_FIRST && !req_wg) load_rows();
+    }
     ReqRun run;
     const int N = scan_requests(p, L, req_wg, run);
     if (req_wg) {
@@ -557,7 +555,6 @@ __global__ __launch_bounds__(kCompileThreads) void compile_kv_kernel(CompilePara
         if (t < p.n_pad) s_slot[threadIdx.x] = token_outputs(p, L, N, t, layer == 0);
     }
     __syncthreads();
-    if (!LOADS_FIRST) load_rows();
     uint8_t* __restrict__ kd = kv.kc[layer];
     uint8_t* __restrict__ vd = kv.vc[layer];
 #pragma unroll
@@ -578,18 +575,26 @@ __global__ __launch_bounds__(kCompileThreads) void compile_kv_kernel(CompilePara
     }
 }
 
-constexpr int kFusedRows = 4;
-constexpr bool kFusedLoadsFirst = true;
-
 bool fused_kv_supported(int row_bytes) { return row_bytes == 1024 || row_bytes == 2048 || row_bytes == 4096; }
 
+// Tile size: two rows per wave (8 tokens per workgroup) when that still gives
+// at least 2048 token workgroups over the layers (eight per compute unit),
+// one row per wave otherwise.  In sweeps on MI355X over 1/2/4 rows per wave,
+// other tile orders and a persistent pipelined grid, this rule was best or
+// within a few percent on every workload: small steps need the extra
+// workgroups (decode-heavy: 13.2 us with one row per wave, 16.5 with four),
+// large ones lose nothing with two rows.
 template <int CPL>
 static void launch_fused(const CompileParams& p_in, const KVParams& kv, int num_layers, hipStream_t s) {
-    constexpr int TT = kFusedRows * (kCompileThreads / kWave);
     CompileParams p = p_in;
+    constexpr int WAVES = kCompileThreads / kWave;
+    const bool two = (int64_t)((p.n_pad + 2 * WAVES - 1) / (2 * WAVES)) * num_layers >= 2048;
+    const int TT = (two ? 2 : 1) * WAVES;
     p.num_token_tiles = (p.n_pad + TT - 1) / TT;
-    hipLaunchKernelGGL((compile_kv_kernel<CPL, kFusedRows, kFusedLoadsFirst>), dim3(p.num_token_tiles + 1, num_layers),
-                       dim3(kCompileThreads), compile_lds_bytes(p.num_reqs, TT), s, p, kv);
+    const dim3 grid(p.num_token_tiles + 1, num_layers);
+    const size_t lds = compile_lds_bytes(p.num_reqs, TT);
+    if (two) hipLaunchKernelGGL((compile_kv_kernel<CPL, 2>), grid, dim3(kCompileThreads), lds, s, p, kv);
+    else hipLaunchKernelGGL((compile_kv_kernel<CPL, 1>), grid, dim3(kCompileThreads), lds, s, p, kv);
 }
 
 hipError_t launch_compile_kv(const CompileParams& p, const KVParams& kv, int num_layers, hipStream_t s) {

@@ -37,8 +37,9 @@ def test_code_digest_ignores_comments_only():
 
 
 def test_kernel_digest_covers_the_kv_code_only():
-    """Edits to other kernels keep the K/V counters valid; an edit to the K/V
-    write's code voids them; a source without the K/V region is an error."""
+    """Edits to other kernels keep a kernel's counters valid; an edit to its
+    own code (or to code it calls) voids them; a source without the region is
+    an error."""
     with open(os.path.join(os.path.dirname(bench.__file__), "ragged_input_compilation_amd", "csrc",
                            "ric_kernels.hip"), encoding="utf-8") as f:
         text = f.read()
@@ -51,6 +52,18 @@ def test_kernel_digest_covers_the_kv_code_only():
     assert kv != text and bench.kernel_source_digest(kv) != base
     with pytest.raises(ValueError):
         bench.kernel_source_digest(text.replace("u32x4 load16(", "u32x4 load_16("))
+    # the single compile + K/V kernel depends on the compile's code and the K/V
+    # helpers too; the compile kernel's own counters only on the compile's code
+    fused = bench.kernel_source_digest(text, "compile_kv")
+    comp = bench.kernel_source_digest(text, "compile")
+    edit_scan = text.replace("const int per = (R + kCompileThreads - 1) / kCompileThreads;",
+                             "const int per = (R + kCompileThreads - 1) / kCompileThreads + 0;", 1)
+    assert edit_scan != text
+    assert bench.kernel_source_digest(edit_scan, "compile_kv") != fused
+    assert bench.kernel_source_digest(edit_scan, "compile") != comp
+    assert bench.kernel_source_digest(edit_scan, "kv") == base
+    assert bench.kernel_source_digest(kv, "compile") == comp
+    assert bench.kernel_source_digest(kv, "compile_kv") != fused
 
 
 def test_load_traffic_needs_matching_code(tmp_path, monkeypatch):
@@ -61,7 +74,7 @@ def test_load_traffic_needs_matching_code(tmp_path, monkeypatch):
     (prof / "kv_chunk_kernel_y_pmc.md").write_text(
         "traffic_bytes_per_launch: 456\nkernel_code_sha256: " + bench.kernel_source_digest() + "\n")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    monkeypatch.setattr(bench, "kernel_source_digest", lambda: bench.code_digest("x"))
+    monkeypatch.setattr(bench, "kernel_source_digest", lambda region="kv": bench.code_digest("x"))
     assert bench.load_traffic("kv_chunk_kernel", "x") is None
     assert bench.load_traffic("kv_chunk_kernel", "missing") is None
     (prof / "kv_chunk_kernel_z_pmc.md").write_text(
@@ -75,3 +88,28 @@ def test_more_than_one_gpu_is_refused(gpus):
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_library_path_rule():
+    """The bench's mirror of the library's choice: one kernel for 1/2/4 KiB
+    rows unless the step averages 1024 or more tokens per request."""
+    assert bench.fused_path(workloads.get("churn"))
+    assert bench.fused_path(workloads.get("mixed"))
+    assert bench.fused_path(workloads.get("decode_heavy"))
+    assert not bench.fused_path(workloads.get("long_context"))
+    assert not bench.fused_path(workloads.get("worked_example"))      # 256 B rows
+    assert bench.dominant_kernel(workloads.get("churn"), 16384) == "compile_kv_kernel"
+    assert bench.dominant_kernel(workloads.get("long_context"), 32768) == "kv_chunk_kernel"
+
+
+def test_cpu_baseline_parallel_equals_single(tmp_path):
+    """The all-cores CPU step (request ranges on threads, then the running
+    totals, compaction and padding) gives the single-thread oracle's outputs;
+    cpu_baseline itself asserts this before timing."""
+    w = workloads.get("worked_example")
+    res = bench.cpu_baseline(w, 0.2)
+    assert res["kind"] == "oracle" and res["cores"] == 1 and res["value"] > 0
+    assert 1 <= res["all_cores"]["cores"] <= min(3, len(os.sched_getaffinity(0)))
+    res = bench.cpu_baseline(workloads.get("mixed"), 0.5)
+    assert 1 <= res["all_cores"]["cores"] <= min(124, len(os.sched_getaffinity(0)))
+    assert res["all_cores"]["value"] > 0

@@ -34,14 +34,14 @@ def _prepare(rt, w):
     return b, exp
 
 
-def _fused_step(rt, w, b, exp, sentinel, host_sources=False, layers=None):
+def _fused_step(rt, w, b, exp, sentinel, host_sources=False, layers=None, flags=0):
     ric, runner = rt
     L = w.num_layers if layers is None else layers
     kc, vc = runner.alloc_caches(w, L, fill=sentinel)
     k, v = runner.alloc_sources(w, exp["n_pad"], seed=w.seed + 29, num_layers=L, host=host_sources)
     kv = runner.KVSet(k, v, kc, vc, w.row_bytes, w.num_kv_blocks * w.block_size)
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    s = runner.compile_and_cache(b, exp["n_pad"], kv, dev_status=status.data_ptr())
+    s = runner.compile_and_cache(b, exp["n_pad"], kv, dev_status=status.data_ptr(), flags=flags)
     torch.cuda.synchronize()
     assert int(status.item()) == 0
     assert (s.num_reqs, s.num_actual_tokens, s.num_tokens_padded) == (exp["num_reqs"], exp["num_actual_tokens"],
@@ -59,13 +59,20 @@ def _check_all(w, exp, kv, sentinel, label):
                               f"{label} layer {l} {nm}")
 
 
-@pytest.mark.parametrize("name", ["worked_example", "decode_heavy", "mixed", "churn", "long_context",
-                                  "long_context_forced"])
-def test_fused_step_matches_oracle(rt, name):
+ALWAYS, NEVER = 1, 2
+CASES = [(n, 0) for n in ("worked_example", "decode_heavy", "mixed", "churn", "long_context", "long_context_forced")] + \
+    [("long_context", ALWAYS), ("long_context_forced", ALWAYS), ("churn", NEVER), ("decode_heavy", NEVER)]
+
+
+@pytest.mark.parametrize("name,flags", CASES, ids=[f"{n}-{f}" for n, f in CASES])
+def test_fused_step_matches_oracle(rt, name, flags):
+    """Each configuration through the library's own choice of path, and the
+    long-context steps forced through the single kernel (the library keeps
+    them on two), churn and decode-heavy forced onto two."""
     w = workloads.get(name)
     b, exp = _prepare(rt, w)
     sentinel = 0x2C3D
-    s, kv = _fused_step(rt, w, b, exp, sentinel)
+    s, kv = _fused_step(rt, w, b, exp, sentinel, flags=flags)
     assert_step_equal(b.step_outputs(s), exp, name)
     _check_all(w, exp, kv, sentinel, name)
     del kv
@@ -103,7 +110,7 @@ def test_fused_random_batches(rt):
         label = f"trial {trial}: B={w.block_size} R={len(w.initial)} row={w.row_bytes} L={w.num_layers}"
         b, exp = _prepare(rt, w)
         sentinel = 0x1357
-        s, kv = _fused_step(rt, w, b, exp, sentinel)
+        s, kv = _fused_step(rt, w, b, exp, sentinel, flags=(0, ALWAYS, NEVER)[trial % 3])
         assert_step_equal(b.step_outputs(s), exp, label)
         _check_all(w, exp, kv, sentinel, label)
         b.close()
@@ -121,15 +128,16 @@ def test_fused_past_one_launch_of_layers(rt):
                            head_dim=128, kv_dtype="bf16", num_layers=40, hidden_size=64, gather="all",
                            initial=reqs, capture_sizes=[N + 5], seed=7)
     b, exp = _prepare(rt, w)
-    s, kv = _fused_step(rt, w, b, exp, 0x0F0F)
+    s, kv = _fused_step(rt, w, b, exp, 0x0F0F, flags=ALWAYS)
     assert_step_equal(b.step_outputs(s), exp, "40 layers")
     _check_all(w, exp, kv, 0x0F0F, "40 layers")
     b.close()
 
 
 def test_fused_equals_separate_calls(rt):
-    """The fused call and ric_compile + ric_reshape_and_cache leave identical
-    caches, null block included when every pad row carries the same bytes."""
+    """The single kernel and ric_compile + ric_reshape_and_cache leave
+    identical caches (mixed has no padded tokens, so the whole cache is
+    deterministic)."""
     ric, runner = rt
     w = workloads.get("mixed")
     caches = []
@@ -140,7 +148,7 @@ def test_fused_equals_separate_calls(rt):
         k, v = runner.alloc_sources(w, n_pad, seed=w.seed + 3)
         kv = runner.KVSet(k, v, kc, vc, w.row_bytes, w.num_kv_blocks * w.block_size)
         if fused:
-            runner.compile_and_cache(b, n_pad, kv)
+            runner.compile_and_cache(b, n_pad, kv, flags=ALWAYS)
         else:
             s = b.compile(n_pad)
             runner.reshape_and_cache(kv, s.slot_mapping, n_pad)
@@ -161,6 +169,7 @@ def test_fused_argument_errors_enqueue_nothing(rt):
     for kw, code in ((dict(row_bytes=24, num_slots=nslots), ric.RIC_EINVAL),
                      (dict(row_bytes=w.row_bytes, num_slots=0), ric.RIC_EINVAL),
                      (dict(row_bytes=w.row_bytes, num_slots=nslots, flags=4), ric.RIC_EINVAL),
+                     (dict(row_bytes=w.row_bytes, num_slots=nslots, flags=3), ric.RIC_EINVAL),
                      (dict(row_bytes=w.row_bytes, num_slots=nslots, src_row_stride=8), ric.RIC_EINVAL)):
         with pytest.raises(ric.RicError) as e:
             ric.ric_compile_and_cache(b.h, exp["n_pad"], *ptrs, **kw)
