@@ -840,9 +840,11 @@ def extra_config(ric, runner, torch, workloads, name, steps, warmup):
     ck = compile_kv_paths(torch, sets, sb, 30, 10, flush_buf)
     del flush_buf
     path = "single_kernel" if fused_path(w0) else "two_kernels"
+    kernel = dominant_kernel(w0, sets[0].n_pad)
     res = {"workload": f"{name}: {DESCRIPTIONS[name]}", "num_reqs": sb["R"], "num_tokens": sb["N"],
            "num_layers": w0.num_layers, "tokens_per_s": sb["N"] / (ms * 1e-3), "ms_per_step": ms,
            "step_bytes": sb["total"], "library_path": path, "compile_plus_kv": ck,
+           "dominant_kernel": kernel, "dominant_kernel_traffic": load_traffic(kernel, name),
            "rotation_instances": len(sets), "seconds": None}
     release(torch, sets)
     res["seconds"] = time.perf_counter() - t0
