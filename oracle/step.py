@@ -90,18 +90,26 @@ def compile_step(rows, *, block_size: int, max_num_reqs: int, max_model_len: int
     for _ in range(R, max_num_reqs):
         qsl.append(N)
 
+    # Every flat token t in [0, N): its request owns the interval
+    # [qsl[i], qsl[i+1]) that holds t; its offset inside that interval, added
+    # to the request's cached length, is its model position; the position
+    # picks the history entry and, split into a block index and an offset
+    # inside the block, the physical K/V slot.
     input_ids: List[int] = []
     positions: List[int] = []
     req_indices: List[int] = []
     slot_mapping: List[int] = []
-    for i, r in enumerate(rows):
-        for j in range(r.num_scheduled):
-            p = r.num_computed + j
-            req_indices.append(i)
-            positions.append(p)
-            input_ids.append(int(r.tokens[p]))
-            logical_block, offset = p // B, p % B
-            slot_mapping.append(int(r.blocks[logical_block]) * B + offset)
+    owner = 0
+    for t in range(N):
+        while qsl[owner + 1] <= t:          # intervals are visited in order
+            owner += 1
+        r = rows[owner]
+        pos = r.num_computed + (t - qsl[owner])
+        block_index, within = divmod(pos, B)
+        req_indices.append(owner)
+        positions.append(pos)
+        input_ids.append(int(r.tokens[pos]))
+        slot_mapping.append(int(r.blocks[block_index]) * B + within)
     for _ in range(N, n_pad):
         input_ids.append(0)
         positions.append(0)

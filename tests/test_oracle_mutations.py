@@ -94,15 +94,16 @@ def _mutant_module(path, old, new, name):
 
 
 PY_MUTANTS = [
-    ("p = r.num_computed + j", "p = j"),                                        # dropped term
-    ("logical_block, offset = p // B, p % B", "logical_block, offset = p % B, p // B"),  # transposed
+    ("pos = r.num_computed + (t - qsl[owner])", "pos = t - qsl[owner]"),       # dropped term
+    ("block_index, within = divmod(pos, B)", "within, block_index = divmod(pos, B)"),  # transposed
+    ("while qsl[owner + 1] <= t:", "while qsl[owner + 1] < t:"),                   # boundary token to the wrong request
     ("logits_indices.append(qsl[i + 1] - 1)", "logits_indices.append(qsl[i + 1])"),     # off by one
     ("1 if r.num_computed + r.num_scheduled < r.num_prompt else 0",
      "1 if r.num_computed + r.num_scheduled <= r.num_prompt else 0"),            # wrong comparison
     ("seq_lens.append(r.num_computed + r.num_scheduled)", "seq_lens.append(r.num_scheduled)"),
-    ("input_ids.append(int(r.tokens[p]))", "input_ids.append(int(r.tokens[j]))"),
-    ("slot_mapping.append(int(r.blocks[logical_block]) * B + offset)",
-     "slot_mapping.append(int(r.blocks[logical_block]) + offset * B)"),
+    ("input_ids.append(int(r.tokens[pos]))", "input_ids.append(int(r.tokens[t - qsl[owner]]))"),
+    ("slot_mapping.append(int(r.blocks[block_index]) * B + within)",
+     "slot_mapping.append(int(r.blocks[block_index]) + within * B)"),
     ("qsl.append(qsl[-1] + r.num_scheduled)", "qsl.append(qsl[-1] + r.num_scheduled - 1)"),
     ("slot_mapping.append(null_block * B)", "slot_mapping.append(-1)"),
     ("for _ in range(R, max_num_reqs):\n        qsl.append(N)", "for _ in range(R, max_num_reqs):\n        qsl.append(0)"),
