@@ -3,7 +3,8 @@
 replaced block rows, condense, decode appends, prefill chunks, a second
 KV-cache group with its own block size, device-side appends of sampled
 tokens, history truncation, device-side corrections of computed counts (some
-with out-of-range accepted counts), and K/V writes.  Every step's compile
+with out-of-range accepted counts), and K/V writes, some of them through the
+single compile + K/V kernel (ric_compile_and_cache).  Every step's compile
 (group 1's slots included), every corrected count and every written cache row
 equals the oracle's."""
 import numpy as np
@@ -19,6 +20,7 @@ MR, M = 24, 256
 POOL = 20000
 BUDGET = 192
 ROW = 64
+ROWF = 1024          # rows the single compile + K/V kernel takes
 
 
 @pytest.fixture(scope="module")
@@ -45,7 +47,11 @@ def test_serving_loop_soak(rt):
     cache = torch.zeros((POOL * B0, ROW), dtype=torch.uint8, device="cuda")
     cache_ref = np.zeros((POOL * B0, ROW), np.uint8)
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    counts = dict(corrections=0, bad_counts=0, kv_writes=0, sampled=0, truncations=0)
+    kf = torch.zeros((POOL * B0, ROWF), dtype=torch.uint8, device="cuda")
+    vf = torch.zeros((POOL * B0, ROWF), dtype=torch.uint8, device="cuda")
+    kf_ref = np.zeros((POOL * B0, ROWF), np.uint8)
+    vf_ref = np.zeros((POOL * B0, ROWF), np.uint8)
+    counts = dict(corrections=0, bad_counts=0, kv_writes=0, sampled=0, truncations=0, fused=0)
 
     def row(rid):
         return ref.rows[ref.row_of[rid]]
@@ -154,7 +160,17 @@ def test_serving_loop_soak(rt):
         step_rows = ref.step_rows()
         want = ref_step.compile_step(step_rows, block_size=B0, max_num_reqs=MR, max_model_len=M,
                                      max_num_batched_tokens=BUDGET, num_kv_blocks=POOL, n_pad=n_pad)
-        s = b.compile(n_pad)
+        fused = rng.random() < 0.25
+        if fused:                                                  # compile + K/V of 1 KiB rows in one kernel
+            srck = rng.integers(0, 256, (n_pad, ROWF), dtype=np.uint8)
+            srcv = rng.integers(0, 256, (n_pad, ROWF), dtype=np.uint8)
+            k_dev, v_dev = torch.from_numpy(srck).cuda(), torch.from_numpy(srcv).cuda()
+            status.zero_()
+            s = ric.ric_compile_and_cache(b.h, n_pad, [k_dev.data_ptr()], [v_dev.data_ptr()], [kf.data_ptr()],
+                                          [vf.data_ptr()], ROWF, POOL * B0, dev_status=status.data_ptr(),
+                                          flags=ric.RIC_FUSE_ALWAYS)
+        else:
+            s = b.compile(n_pad)
         got = b.step_outputs(s)
         for k in ("input_ids", "positions", "req_indices", "slot_mapping", "query_start_loc", "seq_lens",
                   "cu_seqlens_k", "logits_indices", "discard", "sample_indices"):
@@ -164,6 +180,16 @@ def test_serving_loop_soak(rt):
                                             [ref.rows[i].group_blocks[1] for i in range(R)], B1)
         got1 = ric.ric_read_device(s.group_slot_mapping[1], 4 * n_pad, np.int32)
         assert np.array_equal(got1.astype(np.int64), np.asarray(want1, np.int64)), step_no
+
+        if fused:
+            assert int(status.item()) == 0, step_no
+            slots = np.asarray(want["slot_mapping"][:N], np.int64)
+            kf_ref[slots] = srck[:N]
+            vf_ref[slots] = srcv[:N]
+            touched = torch.from_numpy(np.unique(slots)).cuda()
+            assert np.array_equal(kf[touched].cpu().numpy(), kf_ref[touched.cpu().numpy()]), step_no
+            assert np.array_equal(vf[touched].cpu().numpy(), vf_ref[touched.cpu().numpy()]), step_no
+            counts["fused"] += 1
 
         if rng.random() < 0.2:                                     # this step's K/V rows
             src = rng.integers(0, 256, (n_pad, ROW), dtype=np.uint8)
