@@ -21,8 +21,11 @@ def rt():
     return _ric, runner
 
 
-@pytest.mark.parametrize("name", ["worked_example", "mixed"])
-def test_captured_step_replays_match_eager(rt, name):
+@pytest.mark.parametrize("name,single", [("worked_example", False), ("mixed", False), ("mixed", True),
+                                         ("decode_heavy", True)])
+def test_captured_step_replays_match_eager(rt, name, single):
+    """`single`: the step is ric_compile_and_cache (one kernel for these rows)
+    + gather instead of three calls."""
     ric, runner = rt
     w = workloads.get(name)
     side = torch.cuda.Stream()
@@ -42,8 +45,11 @@ def test_captured_step_replays_match_eager(rt, name):
         out = torch.zeros((R, w.hidden_size), dtype=torch.bfloat16, device="cuda")
 
         def step():
-            s = b.compile(n_pad)
-            runner.reshape_and_cache(kv, s.slot_mapping, n_pad, stream=st)
+            if single:
+                s = runner.compile_and_cache(b, n_pad, kv, flags=ric.RIC_FUSE_ALWAYS)
+            else:
+                s = b.compile(n_pad)
+                runner.reshape_and_cache(kv, s.slot_mapping, n_pad, stream=st)
             runner.gather(hidden, s.logits_indices, 0, R, out, stream=st)
             return s
 
@@ -65,7 +71,7 @@ def test_captured_step_replays_match_eager(rt, name):
             for t in kc + vc:
                 t.view(torch.int16).zero_()
             for t in k + v:
-                t.copy_(torch.randn_like(t, dtype=torch.float32).to(t.dtype))
+                t.copy_(torch.randn(t.shape, device=t.device).to(t.dtype))
             hidden.copy_(torch.randn_like(hidden, dtype=torch.float32).to(hidden.dtype))
             out.zero_()
         torch.cuda.synchronize()
@@ -73,13 +79,16 @@ def test_captured_step_replays_match_eager(rt, name):
         torch.cuda.synchronize()
         got = b.step_outputs(s0)
         assert_step_equal(got, exp, f"{name} replay {rep}")
-        for src, cache in ((k[0], kc[0]), (v[0], vc[0])):
-            flat = cache.view(torch.int16).reshape(w.num_kv_blocks * w.block_size, -1)
-            srcf = src.view(torch.int16).reshape(n_pad, -1)
-            assert torch.equal(flat[slots], srcf[:exp["num_actual_tokens"]]), f"{name} replay {rep}: K/V rows"
+        for l in range(w.num_layers):
+            for src, cache in ((k[l], kc[l]), (v[l], vc[l])):
+                flat = cache.view(torch.int16).reshape(w.num_kv_blocks * w.block_size, -1)
+                srcf = src.view(torch.int16).reshape(n_pad, -1)
+                assert torch.equal(flat[slots], srcf[:exp["num_actual_tokens"]]), \
+                    f"{name} replay {rep} layer {l}: K/V rows"
         assert torch.equal(out.view(torch.int16), hidden[logits].view(torch.int16)), f"{name} replay {rep}: gather"
-    del g
+    del g, kv, kc, vc, k, v
     b.close()
+    torch.cuda.empty_cache()
 
 
 def test_capture_with_staged_deltas_is_refused(rt):
