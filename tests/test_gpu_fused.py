@@ -181,3 +181,50 @@ def test_fused_argument_errors_enqueue_nothing(rt):
     torch.cuda.synchronize()
     assert_step_equal(b.step_outputs(s), exp, "after rejected calls")
     b.close()
+
+
+def test_fused_empty_batch_is_all_padding(rt):
+    """No live request: the single kernel writes every padded row to the null
+    block and nothing else; the compile outputs are the padding reading."""
+    ric, runner = rt
+    cfg = ric.make_config(max_num_reqs=4, max_model_len=16, block_size=4, max_blocks_per_req=4,
+                          max_num_batched_tokens=8, num_kv_blocks=10, null_block=3, staging_bytes=0)
+    b = runner.Batch(cfg)
+    ric.ric_schedule(b.h, [], [])
+    row = 1024
+    nslots = 40
+    k = torch.randn((8, row // 2), device="cuda").to(torch.float16)
+    v = torch.randn((8, row // 2), device="cuda").to(torch.float16)
+    kc = torch.full((nslots, row // 2), 77, dtype=torch.int16, device="cuda")
+    vc = torch.full((nslots, row // 2), 77, dtype=torch.int16, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    s = ric.ric_compile_and_cache(b.h, 8, [k.data_ptr()], [v.data_ptr()], [kc.data_ptr()], [vc.data_ptr()], row,
+                                  nslots, dev_status=status.data_ptr(), flags=ric.RIC_FUSE_ALWAYS)
+    torch.cuda.synchronize()
+    got = b.step_outputs(s)
+    assert list(got["slot_mapping"]) == [12] * 8 and list(got["req_indices"]) == [-1] * 8
+    assert list(got["query_start_loc"]) == [0] * 5 and list(got["sample_indices"]) == [-1] * 4
+    assert int(status.item()) == 0
+    others = [i for i in range(nslots) if i != 12]
+    assert bool((kc[others] == 77).all()) and bool((vc[others] == 77).all())
+    # the null slot holds one of the padded rows (which one is not defined)
+    assert any(torch.equal(kc[12], k[t].view(torch.int16)) for t in range(8))
+    b.close()
+
+
+def test_fused_at_the_row_limit(rt):
+    """8000 requests (the row limit: the largest prefix sum a workgroup keeps
+    in LDS) through the single kernel, decodes and short prefills mixed."""
+    rng = np.random.default_rng(8000)
+    reqs = workloads.random_batch(rng, num_reqs=8000, block_size=16, max_model_len=64,
+                                  num_kv_blocks=8000 * 4 + 1, max_q=3, max_c=40)
+    N = sum(r.num_scheduled for r in reqs)
+    w = workloads.Workload("fused_rows", block_size=16, max_num_reqs=8000, max_model_len=64, max_blocks_per_req=4,
+                           max_num_batched_tokens=N + 3, num_kv_blocks=8000 * 4 + 1, kv_heads=4, head_dim=128,
+                           kv_dtype="bf16", num_layers=1, hidden_size=64, gather="all", initial=reqs,
+                           capture_sizes=[N + 3], seed=11)
+    b, exp = _prepare(rt, w)
+    s, kv = _fused_step(rt, w, b, exp, 0x7171, flags=ALWAYS)
+    assert_step_equal(b.step_outputs(s), exp, "8000 rows")
+    _check_all(w, exp, kv, 0x7171, "8000 rows")
+    b.close()
