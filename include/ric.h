@@ -383,10 +383,13 @@ int ric_compile(ric_batch* b, int32_t num_tokens_padded, ric_step* out);
  * layers past 32 use the separate K/V kernel after the compile.  The other
  * K/V arguments are those of ric_reshape_and_cache (k, v, k_cache, v_cache:
  * host arrays of num_layers device pointers; src_row_stride 0 = row_bytes;
- * dev_status optional).  Padded tokens write their rows into the null block,
- * as ric_reshape_and_cache does with the padded slot mapping.  Errors: those
- * of ric_compile and of ric_reshape_and_cache; on an argument error nothing
- * is enqueued. */
+ * dev_status optional; num_slots the cache rows, a slot outside [0,
+ * num_slots) skips its row and counts in *dev_status).  Each source holds
+ * num_tokens_padded rows and must be ready on the handle's stream when the
+ * call is made: the single kernel reads the rows while it compiles.  Padded
+ * tokens write their rows into the null block, as ric_reshape_and_cache does
+ * with the padded slot mapping.  Errors: those of ric_compile and of
+ * ric_reshape_and_cache; on an argument error nothing is enqueued. */
 #define RIC_FUSE_ALWAYS 1u
 #define RIC_FUSE_NEVER  2u
 int ric_compile_and_cache(ric_batch* b, int32_t num_tokens_padded, const void* const* k, const void* const* v,
