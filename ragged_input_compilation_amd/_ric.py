@@ -34,6 +34,7 @@ class RicError(RuntimeError):
 
 RIC_MAX_KV_GROUPS, RIC_SLOTS_PER_TOKEN, RIC_SLOTS_NONE = 4, 0, 1
 RIC_FUSE_ALWAYS, RIC_FUSE_NEVER = 1, 2
+RIC_CHECK_SLOTS_NOALLOC_MAX_SLOTS = 1 << 25
 
 
 class ric_config(ctypes.Structure):

@@ -91,11 +91,28 @@ class Batch:
             self.debug_dump(s)
         return s
 
+    def slot_collisions(self, s: ric.ric_step) -> tuple:
+        """(collisions, out-of-range slots) among the step's real tokens, by
+        the library's device-side check (debugging; synchronises)."""
+        res = torch.zeros(2, dtype=torch.int32, device=self.workspace.device)
+        num_slots = self.cfg.num_kv_blocks * self.cfg.block_size
+        if num_slots <= ric.RIC_CHECK_SLOTS_NOALLOC_MAX_SLOTS:
+            ric.ric_check_slots_noalloc(s.slot_mapping, s.num_tokens_padded, num_slots, res.data_ptr(),
+                                        dev_num_tokens=s.dev_scalars + 4, stream=self.stream)
+        else:
+            nbytes = ric.ric_check_slots_workspace_bytes(num_slots)
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=self.workspace.device)
+            ric.ric_check_slots(s.slot_mapping, s.num_tokens_padded, num_slots, ws.data_ptr(), nbytes,
+                                res.data_ptr(), dev_num_tokens=s.dev_scalars + 4, stream=self.stream)
+        torch.cuda.synchronize()
+        return tuple(int(x) for x in res.tolist())
+
     def debug_dump(self, s: ric.ric_step, limit: int = 32) -> None:
         """Print the small per-step arrays a developer checks first when a step
         goes wrong (request order, counts, boundaries, positions, slots,
-        logits rows, discard), not the tables.  Synchronises: debugging only,
-        enabled by RIC_DEBUG=1."""
+        logits rows, discard), not the tables, and the device-side count of
+        real tokens sharing a slot.  Synchronises: debugging only, enabled by
+        RIC_DEBUG=1."""
         R, n = s.num_reqs, s.num_tokens_padded
         cols = ric.ric_get_columns(self.h)
         show = lambda a: " ".join(str(int(x)) for x in a[:limit]) + (" ..." if len(a) > limit else "")
@@ -109,7 +126,9 @@ class Batch:
         print(f"[ric] seq_lens   {show(self.device_i32(s.seq_lens, R))}")
         print(f"[ric] slots      {show(self.device_i32(s.slot_mapping, n))}")
         print(f"[ric] logits     {show(self.device_i32(s.logits_indices, R))}")
-        print(f"[ric] discard    {show(self.device_u8(s.discard, R))}", flush=True)
+        print(f"[ric] discard    {show(self.device_u8(s.discard, R))}")
+        dup, bad = self.slot_collisions(s)
+        print(f"[ric] slot collisions {dup}, out-of-range slots {bad}", flush=True)
 
     # inspection (tests) ------------------------------------------------------
     def device_i32(self, ptr: int, n: int) -> np.ndarray:

@@ -717,4 +717,22 @@ def test_debug_dump_prints_the_step(rt, capsys):
     assert "[ric] seq_lens   7 6 22\n" in out
     assert "[ric] logits     6 7 19\n" in out
     assert "[ric] positions  0 1 2 3 4 5 6 5 10 11" in out
+    assert "[ric] slot collisions 0, out-of-range slots 0" in out
+    b.close()
+
+
+def test_debug_check_finds_a_planted_collision(rt):
+    """The debug check counts a slot shared by two real tokens: the worked
+    example's slot list with token 5 redirected to token 4's slot."""
+    ric, runner = rt
+    w = workloads.get("worked_example")
+    b, s, ref, order, exp, _ = _compile(rt, w)
+    assert b.slot_collisions(s) == (0, 0)
+    slots = torch.from_numpy(np.asarray(exp["slot_mapping"], np.int32)).cuda()
+    slots[5] = slots[4]
+    fake = ric.ric_step()
+    fake.slot_mapping = slots.data_ptr()
+    fake.num_tokens_padded = exp["n_pad"]
+    fake.dev_scalars = s.dev_scalars
+    assert b.slot_collisions(fake) == (1, 0)
     b.close()
