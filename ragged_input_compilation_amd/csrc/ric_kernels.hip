@@ -1,7 +1,8 @@
-// HIP kernels for gfx950 (CDNA4, wave64): step compile, paged K/V write,
-// row gather, condense row move, staged-delta apply, and the small kernels of
-// the next rows (padded tables, speculative-decoding indices, sampled-token
-// append, correction of optimistic computed counts).
+// HIP kernels for gfx950 (CDNA4, wave64): step compile, paged K/V write, the
+// two in one kernel, row gather, condense row move, staged-delta apply, the
+// slot-collision check, and the small kernels of the next rows (padded
+// tables, speculative-decoding indices, sampled-token append, correction of
+// optimistic computed counts).
 //
 // Sources (page title, section):
 //   [P1] "vLLM 源码完全拆解（五）：GPUModelRunner 如何把动态请求拼成一次 GPU 前向"
