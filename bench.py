@@ -4,7 +4,8 @@
 One step = compile the persistent batch into the flat token stream and its
 metadata and write the step's K/V rows into the paged caches of every layer
 (one library call, ric_compile_and_cache: a single kernel, or the compile and
-the K/V kernel when the step is mostly long chunks), then gather the hidden
+the K/V kernel for steps of long chunks and rows that kernel does not take),
+then gather the hidden
 rows that produce logits.  Inputs (column store, K/V sources, hidden states)
 are resident in HBM before the timed region.  Steps rotate over independently
 seeded instances of the same configuration (different block tables, token
@@ -98,9 +99,9 @@ def kv_kernel_name(w, n_tokens):
 
 
 def fused_path(w):
-    """Whether ric_compile_and_cache takes the single kernel for this step
-    (mirrors the library's rule: 1, 2 or 4 KiB rows, and fewer than 1024
-    scheduled tokens per request on average)."""
+    """Whether ric_compile_and_cache takes the single kernel for this step by
+    the library's own choice (mirrors its rule: rows of 1, 2 or 4 KiB, and
+    fewer than 1024 scheduled tokens per request on average)."""
     live = w.live_requests()
     N = sum(r.num_scheduled for r in live)
     return w.row_bytes in (1024, 2048, 4096) and N < 1024 * max(len(live), 1)

@@ -1208,19 +1208,21 @@ int ric_compile_and_cache(ric_batch* b, int32_t n_pad, const void* const* k, con
     if (rc) return rc;
     const CompileParams p = compile_params(b, n_pad);
     kv.slot = b->d_slot;
-    // The library's own choice: one kernel unless the step is mostly long
-    // per-request runs (on average 1024 or more tokens per request), where the
-    // K/V kernel's small tiles stream contiguous rows at the copy ceiling and
-    // the fused kernel's wave rows measured up to 15% slower on some machines
-    // (long-context: 52 vs 46 us for the copy alone).
-    bool fuse = path == RIC_FUSE_ALWAYS ||
-                (path == 0 && (int64_t)b->sched_N < (int64_t)1024 * std::max<int32_t>(b->sched_R, 1));
-    fuse = fuse && num_layers > 0 && n_pad > 0 && fused_kv_supported(row_bytes);
+    // A step whose scheduled tokens average 1024 or more per request is mostly
+    // long contiguous runs.  The library's own choice keeps those on the
+    // compile kernel followed by the K/V kernel's small streaming tiles: the
+    // single kernel's tile shape for them is faster with warm caches
+    // (long-context 47.7 against 50.2 us) but slower after the caches were
+    // flushed (56.2 against 51.0 us), where the two kernels measured the same
+    // either way.  Other steps take the single kernel.
+    const bool long_runs = (int64_t)b->sched_N >= (int64_t)1024 * std::max<int32_t>(b->sched_R, 1);
+    const bool fuse = (path == RIC_FUSE_ALWAYS || (path == 0 && !long_runs)) && num_layers > 0 && n_pad > 0 &&
+                      fused_kv_supported(row_bytes);
     int32_t done = 0;
     if (fuse) {
         done = std::min<int32_t>(kMaxLayersPerLaunch, num_layers);
         set_layers(&kv, k, v, k_cache, v_cache, 0, done);
-        HIP_TRY(launch_compile_kv(p, kv, done, b->stream));
+        HIP_TRY(launch_compile_kv(p, kv, done, long_runs, b->stream));
     } else {
         HIP_TRY(launch_compile(p, b->stream));
     }

@@ -167,9 +167,12 @@ hipError_t launch_append_sampled(int32_t* tokens, const int64_t* dst_off, const 
 
 // Compile plus the K/V write of `num_layers` (<= kMaxLayersPerLaunch) layers
 // through the group-0 slots in one launch; only for rows the fused kernel
-// handles (fused_kv_supported).  p.num_token_tiles is set by the launcher.
+// handles (fused_kv_supported).  `long_runs`: the step is mostly long
+// per-request runs (picks the tile shape).  p.num_token_tiles is set by the
+// launcher.
 bool fused_kv_supported(int row_bytes);
-hipError_t launch_compile_kv(const CompileParams& p, const KVParams& kv, int num_layers, hipStream_t s);
+hipError_t launch_compile_kv(const CompileParams& p, const KVParams& kv, int num_layers, bool long_runs,
+                             hipStream_t s);
 
 // Clears ceil(num_slots / 32) bitmap words, then counts, for the first
 // min(n, *dev_n) slots (n when dev_n is null), collisions in result[0] and

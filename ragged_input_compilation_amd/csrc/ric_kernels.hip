@@ -505,17 +505,19 @@ hipError_t launch_kv_scatter(const KVParams& p_in, int num_layers, hipStream_t s
 // ---------------------------------------------------------------------------
 // Compile and K/V write in one launch.  blockIdx.y = layer; workgroup x <
 // num_token_tiles owns TT = ROWS * 4 consecutive tokens, the last one (layer 0
-// only) writes the per-request outputs.  Each token workgroup first issues
-// the loads of its tokens' K and V rows of its layer (they do not depend on
-// the compile), then rebuilds query_start_loc in LDS like the compile kernel,
-// derives its tokens' slots (layer-0 workgroups also write the per-token
-// outputs) and stores the rows, wave by wave as the wave kernel does.  This
-// saves the second launch and the drain between two kernels, and the loads of
-// a tile overlap its slot work.  A slot outside [0, num_slots) skips its row
-// and counts in *status, as in the K/V kernels.
+// only) writes the per-request outputs.  Each token workgroup issues the
+// loads of the first PRE rows of each wave's K and V rows of its layer (they
+// do not depend on the compile), rebuilds query_start_loc in LDS like the
+// compile kernel, derives its tokens' slots (layer-0 workgroups also write the
+// per-token outputs), loads the remaining rows and stores them all, wave by
+// wave as the wave kernel does.  This saves the second launch and the drain
+// between two kernels, and the first rows' loads overlap the slot work.  A
+// slot outside [0, num_slots) skips its row and counts in *status, as in the
+// K/V kernels.
 // ---------------------------------------------------------------------------
-template <int CPL, int ROWS>
+template <int CPL, int ROWS, int PRE>
 __global__ __launch_bounds__(kCompileThreads) void compile_kv_kernel(CompileParams p, KVParams kv) {
+    static_assert(PRE >= 0 && PRE <= ROWS, "rows loaded early must be rows of the wave");
     constexpr int WAVES = kCompileThreads / kWave;
     constexpr int TT = ROWS * WAVES;
     extern __shared__ int32_t smem[];
@@ -528,22 +530,23 @@ __global__ __launch_bounds__(kCompileThreads) void compile_kv_kernel(CompilePara
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int tile0 = blockIdx.x * TT;
     const int t0 = tile0 + wid * ROWS;         // this wave's first row
+    const uint8_t* __restrict__ ks = kv.k[layer];
+    const uint8_t* __restrict__ vs = kv.v[layer];
     u32x4 a[ROWS][2 * CPL];
-    if (!req_wg) {
-        const uint8_t* __restrict__ ks = kv.k[layer];
-        const uint8_t* __restrict__ vs = kv.v[layer];
+    auto load_row = [&](int r) {
+        const int t = t0 + r;
+        if (t < p.n_pad) {
+            const int64_t so = (int64_t)t * kv.src_stride + lane * 16;
 #pragma unroll
-        for (int r = 0; r < ROWS; ++r) {
-            const int t = t0 + r;
-            if (t < p.n_pad) {
-                const int64_t so = (int64_t)t * kv.src_stride + lane * 16;
-#pragma unroll
-                for (int c = 0; c < CPL; ++c) {
-                    a[r][c] = load16<true>(ks + so + c * 1024);
-                    a[r][CPL + c] = load16<true>(vs + so + c * 1024);
-                }
+            for (int c = 0; c < CPL; ++c) {
+                a[r][c] = load16<true>(ks + so + c * 1024);
+                a[r][CPL + c] = load16<true>(vs + so + c * 1024);
             }
         }
+    };
+    if (!req_wg) {
+#pragma unroll
+        for (int r = 0; r < PRE; ++r) load_row(r);
     }
     ReqRun run;
     const int N = scan_requests(p, L, req_wg, run);
@@ -556,6 +559,8 @@ __global__ __launch_bounds__(kCompileThreads) void compile_kv_kernel(CompilePara
         if (t < p.n_pad) s_slot[threadIdx.x] = token_outputs(p, L, N, t, layer == 0);
     }
     __syncthreads();
+#pragma unroll
+    for (int r = PRE; r < ROWS; ++r) load_row(r);
     uint8_t* __restrict__ kd = kv.kc[layer];
     uint8_t* __restrict__ vd = kv.vc[layer];
 #pragma unroll
@@ -578,31 +583,38 @@ __global__ __launch_bounds__(kCompileThreads) void compile_kv_kernel(CompilePara
 
 bool fused_kv_supported(int row_bytes) { return row_bytes == 1024 || row_bytes == 2048 || row_bytes == 4096; }
 
-// Tile size: two rows per wave (8 tokens per workgroup) when that still gives
-// at least 2048 token workgroups over the layers (eight per compute unit),
-// one row per wave otherwise.  In sweeps on MI355X over 1/2/4 rows per wave,
-// other tile orders and a persistent pipelined grid, this rule was best or
-// within a few percent on every workload: small steps need the extra
-// workgroups (decode-heavy: 13.2 us with one row per wave, 16.5 with four),
-// large ones lose nothing with two rows.
+// Tile shape, from sweeps on MI355X over 1/2/4/8 rows per wave, rows loaded
+// before or after the prefix sum, other tile orders and a persistent grid.
+// Steps of long per-request runs (few requests: a short prefix sum) take two
+// rows per wave and load only the first before the prefix sum: loading every
+// row up front puts more reads in flight than some machines serve well
+// (long-context: 48 us against 52 us all-first, and 50 us for the compile and
+// the K/V kernel as two launches).  Other steps load every row first, so the
+// longer prefix sum over many requests hides behind them, with two rows per
+// wave when that still gives at least 2048 token workgroups over the layers
+// (eight per compute unit) and one otherwise (decode-heavy: 13.2 us with one
+// row per wave, 16.5 with four).
 template <int CPL>
-static void launch_fused(const CompileParams& p_in, const KVParams& kv, int num_layers, hipStream_t s) {
+static void launch_fused(const CompileParams& p_in, const KVParams& kv, int num_layers, bool long_runs,
+                         hipStream_t s) {
     CompileParams p = p_in;
     constexpr int WAVES = kCompileThreads / kWave;
-    const bool two = (int64_t)((p.n_pad + 2 * WAVES - 1) / (2 * WAVES)) * num_layers >= 2048;
+    const bool two = long_runs || (int64_t)((p.n_pad + 2 * WAVES - 1) / (2 * WAVES)) * num_layers >= 2048;
     const int TT = (two ? 2 : 1) * WAVES;
     p.num_token_tiles = (p.n_pad + TT - 1) / TT;
     const dim3 grid(p.num_token_tiles + 1, num_layers);
     const size_t lds = compile_lds_bytes(p.num_reqs, TT);
-    if (two) hipLaunchKernelGGL((compile_kv_kernel<CPL, 2>), grid, dim3(kCompileThreads), lds, s, p, kv);
-    else hipLaunchKernelGGL((compile_kv_kernel<CPL, 1>), grid, dim3(kCompileThreads), lds, s, p, kv);
+    if (long_runs) hipLaunchKernelGGL((compile_kv_kernel<CPL, 2, 1>), grid, dim3(kCompileThreads), lds, s, p, kv);
+    else if (two) hipLaunchKernelGGL((compile_kv_kernel<CPL, 2, 2>), grid, dim3(kCompileThreads), lds, s, p, kv);
+    else hipLaunchKernelGGL((compile_kv_kernel<CPL, 1, 1>), grid, dim3(kCompileThreads), lds, s, p, kv);
 }
 
-hipError_t launch_compile_kv(const CompileParams& p, const KVParams& kv, int num_layers, hipStream_t s) {
+hipError_t launch_compile_kv(const CompileParams& p, const KVParams& kv, int num_layers, bool long_runs,
+                             hipStream_t s) {
     if (num_layers < 1 || !fused_kv_supported(kv.row_bytes)) return hipErrorInvalidValue;
-    if (kv.row_bytes == 1024) launch_fused<1>(p, kv, num_layers, s);
-    else if (kv.row_bytes == 2048) launch_fused<2>(p, kv, num_layers, s);
-    else launch_fused<4>(p, kv, num_layers, s);
+    if (kv.row_bytes == 1024) launch_fused<1>(p, kv, num_layers, long_runs, s);
+    else if (kv.row_bytes == 2048) launch_fused<2>(p, kv, num_layers, long_runs, s);
+    else launch_fused<4>(p, kv, num_layers, long_runs, s);
     return hipGetLastError();
 }
 

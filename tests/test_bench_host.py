@@ -93,13 +93,13 @@ def test_more_than_one_gpu_is_refused(gpus):
 def test_library_path_rule():
     """The bench's mirror of the library's choice: one kernel for 1/2/4 KiB
     rows unless the step averages 1024 or more tokens per request."""
-    assert bench.fused_path(workloads.get("churn"))
-    assert bench.fused_path(workloads.get("mixed"))
-    assert bench.fused_path(workloads.get("decode_heavy"))
+    for name in ("churn", "mixed", "decode_heavy"):
+        assert bench.fused_path(workloads.get(name)), name
     assert not bench.fused_path(workloads.get("long_context"))
     assert not bench.fused_path(workloads.get("worked_example"))      # 256 B rows
     assert bench.dominant_kernel(workloads.get("churn"), 16384) == "compile_kv_kernel"
     assert bench.dominant_kernel(workloads.get("long_context"), 32768) == "kv_chunk_kernel"
+    assert bench.dominant_kernel(workloads.get("worked_example"), 32) == "kv_chunk_kernel"
 
 
 def test_cpu_baseline_parallel_equals_single(tmp_path):

@@ -61,14 +61,16 @@ def _check_all(w, exp, kv, sentinel, label):
 
 ALWAYS, NEVER = 1, 2
 CASES = [(n, 0) for n in ("worked_example", "decode_heavy", "mixed", "churn", "long_context", "long_context_forced")] + \
-    [("long_context", ALWAYS), ("long_context_forced", ALWAYS), ("churn", NEVER), ("decode_heavy", NEVER)]
+    [("long_context", ALWAYS), ("long_context_forced", ALWAYS), ("mixed", NEVER), ("churn", NEVER),
+     ("decode_heavy", NEVER)]
 
 
 @pytest.mark.parametrize("name,flags", CASES, ids=[f"{n}-{f}" for n, f in CASES])
 def test_fused_step_matches_oracle(rt, name, flags):
-    """Each configuration through the library's own choice of path, and the
-    long-context steps forced through the single kernel (the library keeps
-    them on two), churn and decode-heavy forced onto two."""
+    """Each configuration through the library's own choice of path, the
+    long-context steps forced onto the single kernel (its long-run tile
+    shape), the others forced onto the compile kernel followed by the K/V
+    kernel."""
     w = workloads.get(name)
     b, exp = _prepare(rt, w)
     sentinel = 0x2C3D
@@ -228,3 +230,36 @@ def test_fused_at_the_row_limit(rt):
     assert_step_equal(b.step_outputs(s), exp, "8000 rows")
     _check_all(w, exp, kv, 0x7171, "8000 rows")
     b.close()
+
+
+def test_fused_long_runs(rt):
+    """Steps of long per-request runs (1024 or more scheduled tokens per
+    request on average), alternately through the single kernel's long-run
+    tile shape and the library's own choice (two kernels), 24 seeded
+    batches: 1-8 requests, chunks of 1024-4096 tokens on cached prefixes up to
+    4000, block sizes 1, 16, 64 and 100, rows of 1, 2 and 4 KiB, 1-3 layers,
+    padded tails; every output and cache byte against the oracle."""
+    rng = np.random.default_rng(1024)
+    for trial in range(24):
+        B = int(rng.choice([1, 16, 64, 100]))
+        R = int(rng.integers(1, 9))
+        M = 8192
+        pool = R * -(-M // B) + 10
+        reqs = workloads.random_batch(rng, num_reqs=R, block_size=B, max_model_len=M, num_kv_blocks=pool,
+                                      max_q=4096, max_c=4000)
+        N = sum(r.num_scheduled for r in reqs)
+        if N < 1024 * R:                    # not a long-run step: drawn again in the next trial
+            continue
+        heads = (4, 8, 16)[trial % 3]
+        n_pad = N + int(rng.integers(0, 40))
+        w = workloads.Workload("long_runs", block_size=B, max_num_reqs=R + 2, max_model_len=M,
+                               max_blocks_per_req=-(-M // B), max_num_batched_tokens=n_pad, num_kv_blocks=pool,
+                               kv_heads=heads, head_dim=128, kv_dtype="bf16", num_layers=1 + trial % 3,
+                               hidden_size=64, gather="all", initial=reqs, capture_sizes=[n_pad],
+                               seed=int(rng.integers(1 << 30)))
+        label = f"trial {trial}: B={B} R={R} N={N} row={w.row_bytes} L={w.num_layers}"
+        b, exp = _prepare(rt, w)
+        s, kv = _fused_step(rt, w, b, exp, 0x5A5A, flags=(ALWAYS, 0)[trial % 2])
+        assert_step_equal(b.step_outputs(s), exp, label)
+        _check_all(w, exp, kv, 0x5A5A, label)
+        b.close()
