@@ -507,7 +507,8 @@ hipError_t launch_kv_scatter(const KVParams& p_in, int num_layers, hipStream_t s
 // num_token_tiles owns TT = ROWS * 4 consecutive tokens, the last one (layer 0
 // only) writes the per-request outputs.  Each token workgroup issues the
 // loads of the first PRE rows of each wave's K and V rows of its layer (they
-// do not depend on the compile), rebuilds query_start_loc in LDS like the
+// do not depend on the compile; with at most 256 requests the request
+// counters are loaded just before them), rebuilds query_start_loc in LDS like the
 // compile kernel, derives its tokens' slots (layer-0 workgroups also write the
 // per-token outputs), loads the remaining rows and stores them all, wave by
 // wave as the wave kernel does.  This saves the second launch and the drain
@@ -515,6 +516,39 @@ hipError_t launch_kv_scatter(const KVParams& p_in, int num_layers, hipStream_t s
 // slot outside [0, num_slots) skips its row and counts in *status, as in the
 // K/V kernels.
 // ---------------------------------------------------------------------------
+// Steps of at most kCompileThreads requests: thread i's own request's q and c,
+// which a token workgroup of the single compile + K/V kernel loads before its
+// K/V rows, so that these loads are not queued behind the rows.
+struct OwnCounters {
+    int q, c;
+};
+
+__device__ __forceinline__ OwnCounters load_own_counters(const CompileParams& p) {
+    OwnCounters oc{0, 0};
+    const int i = threadIdx.x;
+    if (i < p.num_reqs) {
+        oc.q = p.scal[(int64_t)kNumScheduled * p.max_num_reqs + i];
+        oc.c = p.scal[(int64_t)kNumComputed * p.max_num_reqs + i];
+    }
+    return oc;
+}
+
+// scan_requests for a token workgroup whose counters were loaded by
+// load_own_counters.  Contains barriers: every thread must call it.
+__device__ __forceinline__ int scan_own_counters(const CompileParams& p, const CompileLds& L, OwnCounters oc) {
+    const int i = threadIdx.x;
+    const int R = p.num_reqs;
+    int N = 0;
+    const int off = block_exclusive_scan<kCompileThreads>(i < R ? oc.q : 0, L.tmp, &N);
+    if (i < R) {
+        L.qsl[i] = off;
+        L.base[i] = oc.c - off;
+    }
+    if (i == 0) L.qsl[R] = N;
+    __syncthreads();
+    return N;
+}
+
 template <int CPL, int ROWS, int PRE>
 __global__ __launch_bounds__(kCompileThreads) void compile_kv_kernel(CompileParams p, KVParams kv) {
     static_assert(PRE >= 0 && PRE <= ROWS, "rows loaded early must be rows of the wave");
@@ -544,12 +578,16 @@ __global__ __launch_bounds__(kCompileThreads) void compile_kv_kernel(CompilePara
             }
         }
     };
+    // up to kCompileThreads requests, each thread's counters go out before the rows
+    const bool own = !req_wg && p.num_reqs <= kCompileThreads;
+    OwnCounters oc{0, 0};
+    if (own) oc = load_own_counters(p);
     if (!req_wg) {
 #pragma unroll
         for (int r = 0; r < PRE; ++r) load_row(r);
     }
     ReqRun run;
-    const int N = scan_requests(p, L, req_wg, run);
+    const int N = own ? scan_own_counters(p, L, oc) : scan_requests(p, L, req_wg, run);
     if (req_wg) {
         request_outputs(p, run, L, N);
         return;
