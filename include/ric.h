@@ -379,9 +379,10 @@ int ric_compile(ric_batch* b, int32_t num_tokens_padded, ric_step* out);
  * flags picks the path: 0 lets the library choose (the single kernel,
  * except for steps whose scheduled tokens average 1024 or more per request:
  * those long contiguous runs go through the compile kernel and the K/V
- * kernel, which measured faster once the caches are cold), RIC_FUSE_ALWAYS
- * asks for the single kernel (with a tile shape of its own for long runs,
- * faster when caches are warm), RIC_FUSE_NEVER for the two kernels; any
+ * kernel, which measured faster whenever other kernels ran just before),
+ * RIC_FUSE_ALWAYS asks for the single kernel (with a tile shape of its own
+ * for long runs, faster only in calls made back to back), RIC_FUSE_NEVER for
+ * the two kernels; any
  * other bit is EINVAL.  Other row sizes and layers past 32 use
  * the separate K/V kernel after the compile.  The other
  * K/V arguments are those of ric_reshape_and_cache (k, v, k_cache, v_cache:

@@ -1211,10 +1211,11 @@ int ric_compile_and_cache(ric_batch* b, int32_t n_pad, const void* const* k, con
     // A step whose scheduled tokens average 1024 or more per request is mostly
     // long contiguous runs.  The library's own choice keeps those on the
     // compile kernel followed by the K/V kernel's small streaming tiles: the
-    // single kernel's tile shape for them is faster with warm caches
-    // (long-context 47.7 against 50.2 us) but slower after the caches were
-    // flushed (56.2 against 51.0 us), where the two kernels measured the same
-    // either way.  Other steps take the single kernel.
+    // single kernel's tile shape for them is faster only when it runs right
+    // after itself (long-context 46.7 against 50.3 us) and slower after any
+    // other kernel (55-57 us after a read, a matrix product or an idle gap,
+    // 70 us after a large write), while the two kernels take 51 us in every
+    // case.  Other steps take the single kernel.
     const bool long_runs = (int64_t)b->sched_N >= (int64_t)1024 * std::max<int32_t>(b->sched_R, 1);
     const bool fuse = (path == RIC_FUSE_ALWAYS || (path == 0 && !long_runs)) && num_layers > 0 && n_pad > 0 &&
                       fused_kv_supported(row_bytes);
