@@ -182,9 +182,11 @@ const char* ric_last_error(void);
 
 /* ---- column-store deltas ([P1 §新请求建立完整状态], [P1 §驻留请求只合并差量],
  *      [P2 §8.2.2 三种变更操作]).  Each call updates the host mirror at once and
- *      stages its payload; staged payloads reach the device column store in one
- *      upload plus one scatter kernel at the next flush (explicit ric_flush,
- *      ric_condense or ric_compile, or when staging fills). */
+ *      stages its payload; staged payloads reach the device column store at
+ *      the next flush (explicit ric_flush, ric_condense or ric_compile, or when
+ *      staging fills) through one scatter kernel, which reads a log of up to
+ *      64 KiB straight from the pinned host staging and a larger one after
+ *      one copy into device staging. */
 
 /* Install a new request in the lowest free row: token history tokens[0,T),
  * prompt length, computed count, block ids blocks[0,nb) (each in

@@ -737,14 +737,26 @@ hipError_t launch_move_rows(const MoveParams& p, int max_token_chunks, hipStream
 }
 
 // ---------------------------------------------------------------------------
-// Staged deltas: one workgroup per op copies its words from the uploaded
-// payload to the column store.  Ops of one flush never overlap.
+// Staged deltas: one workgroup per op copies its words from the flush's log
+// (pinned host memory read in place, or its copy in device staging) to the
+// column store.  Ops of one flush never overlap.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void apply_deltas_kernel(const uint32_t* payload, const DeltaOp* ops) {
     const DeltaOp op = ops[blockIdx.x];
     uint32_t* dst = reinterpret_cast<uint32_t*>(op.dst);
     const uint32_t* src = payload + op.src_word;
-    for (uint32_t w = threadIdx.x; w < op.n_words; w += 256) dst[w] = src[w];
+    // eight loads in flight per lane: the payload may be read from pinned host
+    // memory, where each pass costs a round trip over the host link
+    constexpr uint32_t U = 8;
+    for (uint32_t base = threadIdx.x; base < op.n_words; base += 256 * U) {
+        uint32_t v[U];
+#pragma unroll
+        for (uint32_t u = 0; u < U; ++u)
+            if (base + u * 256 < op.n_words) v[u] = src[base + u * 256];
+#pragma unroll
+        for (uint32_t u = 0; u < U; ++u)
+            if (base + u * 256 < op.n_words) dst[base + u * 256] = v[u];
+    }
 }
 
 hipError_t launch_apply_deltas(const uint32_t* payload, const DeltaOp* ops, int n_ops, hipStream_t s) {

@@ -44,6 +44,10 @@ hipError_t hipFree(void* ptr) {
 }
 hipError_t hipHostMalloc(void** ptr, size_t size, unsigned int) { return hipMalloc(ptr, size); }
 hipError_t hipHostFree(void* ptr) { return hipFree(ptr); }
+hipError_t hipHostGetDevicePointer(void** dptr, void* hptr, unsigned int) {
+    *dptr = hptr;
+    return hipSuccess;
+}
 hipError_t hipMemcpy(void* dst, const void* src, size_t n, hipMemcpyKind) {
     std::memcpy(dst, src, n);
     return hipSuccess;
