@@ -655,8 +655,10 @@ def next_rows(ric, runner, torch, w, st, reps=20):
     nbytes = 4 * R + 4 * sum(nb) + 4 * R * width
     out["padded_block_table"] = dict(rows=R, width=width, us=us, bytes=nbytes, gbps=nbytes / (us * 1e-6) / 1e9)
 
+    # host arrays built once, as a runner keeps them, so the events time the
+    # library's calls rather than Python list conversion
     q = [by_id[i].num_scheduled for i in order]
-    d = [min(x - 1, 3) for x in q]
+    d = np.asarray([min(x - 1, 3) for x in q], np.int32)
     m = ric.ric_spec_decode_metadata(h, d)
     us = timed(lambda: ric.ric_spec_decode_metadata(h, d))
     nbytes = 4 * R + 4 * (R + 1) + 4 * m.num_draft_tokens + 4 * m.num_logits + 4 * (R + 1) + \
@@ -665,10 +667,11 @@ def next_rows(ric, runner, torch, w, st, reps=20):
 
     b2 = runner.Batch(runner.config_of(w))
     b2.load_history(w)
-    rows = [r for r, rid in enumerate(b2.row_order()) if len(by_id[rid].tokens) + reps + 2 <= w.max_model_len]
-    if rows:
+    rows = np.asarray([r for r, rid in enumerate(b2.row_order())
+                       if len(by_id[rid].tokens) + reps + 2 <= w.max_model_len], np.int32)
+    if len(rows):
         sampled = torch.randint(0, 1 << 20, (len(rows),), dtype=torch.int32, device="cuda")
-        src = list(reversed(range(len(rows))))
+        src = np.arange(len(rows) - 1, -1, -1, dtype=np.int32)
         us = timed(lambda: ric.ric_append_sampled(b2.h, rows, sampled.data_ptr(), len(rows), src))
         out["append_sampled"] = dict(rows=len(rows), us_per_call=us, bytes=20 * len(rows))
     else:
@@ -681,8 +684,6 @@ def next_rows(ric, runner, torch, w, st, reps=20):
     b4 = runner.Batch(runner.config_of(w))
     b4.load_history(w)
     order4 = b4.row_order()
-    # host arrays built once, as a runner keeps them, so the events time the
-    # library's calls rather than Python list conversion
     c4 = np.asarray([by_id[i].num_computed for i in order4], np.int32)
     q4 = np.asarray([by_id[i].num_scheduled for i in order4], np.int32)
     d4 = np.minimum(c4, 3).astype(np.int32)
@@ -831,9 +832,10 @@ def compile_kv_paths(torch, sets, sb, reps, cold_reps, flush_buf):
     return out
 
 
-def extra_config(ric, runner, torch, workloads, name, steps, warmup):
+def extra_config(ric, runner, torch, workloads, name, steps, warmup, with_next_rows=False):
     """Another configuration measured the same way as the headline (fewer
-    diagnostics): whole-step tokens/s, and compile + K/V by both paths."""
+    diagnostics): whole-step tokens/s, and compile + K/V by both paths; with
+    `with_next_rows`, also the calls beyond the step (next_rows)."""
     t0 = time.perf_counter()
     w0, sb, sets = build_sets(ric, runner, torch, workloads, name)
     ms = timed_steps(torch, sets, steps, warmup)
@@ -847,6 +849,8 @@ def extra_config(ric, runner, torch, workloads, name, steps, warmup):
            "step_bytes": sb["total"], "library_path": path, "compile_plus_kv": ck,
            "dominant_kernel": kernel, "dominant_kernel_traffic": load_traffic(kernel, name),
            "rotation_instances": len(sets), "seconds": None}
+    if with_next_rows and name != "worked_example":
+        res["next_rows"] = next_rows(ric, runner, torch, w0, sets[0])
     release(torch, sets)
     res["seconds"] = time.perf_counter() - t0
     return res
@@ -946,7 +950,7 @@ def main():
         for name in EXTRA_CONFIGS:
             if name != args.config:
                 configs[name] = extra_config(ric, runner, torch, workloads, name, max(args.steps, 50),
-                                             max(args.warmup, 10))
+                                             max(args.warmup, 10), with_next_rows=not args.no_diagnostics)
 
     N = sb["N"]
     ceiling = diag.get("copy_ceiling")
