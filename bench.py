@@ -408,12 +408,14 @@ class _CpuStep:
 
 
 class _CpuParallel:
-    """The same step split by requests over a pool of threads: thread k
+    """The same step on a pool of threads, in two phases: thread k < R
     compiles one contiguous range of requests (balanced by scheduled tokens)
-    as a batch of its own, shifts its range's request-relative outputs into
-    place, and writes its range's K/V rows; the main thread then fills in the
-    running totals across ranges, the compacted sample list, the padding and
-    the gather.  The C calls release the interpreter lock."""
+    as a batch of its own and shifts its range's request-relative outputs into
+    place; after a barrier every thread of the pool writes the K/V rows of
+    one contiguous range of tokens (the bulk of the work, independent of the
+    request count); the main thread then fills in the running totals across
+    ranges, the compacted sample list, the padding and the gather.  The C
+    calls release the interpreter lock."""
 
     def __init__(self, cs, threads):
         np = cs.np
@@ -437,28 +439,36 @@ class _CpuParallel:
                                 ctypes.cast(cs.disc.ctypes.data + r0, ctypes.POINTER(ctypes.c_uint8)),
                                 p(loc["smp"]), 0, 0, 0, 0)
             self.locals.append((loc, ins, out))
-        self.threads_used = len(self.ranges)
-        self.start = threading.Barrier(self.threads_used + 1)
-        self.done = threading.Barrier(self.threads_used + 1)
+        self.threads_used = max(1, threads)
+        self.compile_threads = len(self.ranges)
+        P = self.threads_used
+        self.tranges = [(cs.N * k // P, cs.N * (k + 1) // P) for k in range(P)]
+        self.start = threading.Barrier(P + 1)
+        self.mid = threading.Barrier(P)
+        self.done = threading.Barrier(P + 1)
         self.stop = False
-        self.workers = [threading.Thread(target=self._work, args=(k,), daemon=True) for k in range(self.threads_used)]
+        self.workers = [threading.Thread(target=self._work, args=(k,), daemon=True) for k in range(P)]
         for t in self.workers:
             t.start()
 
     def _work(self, k):
         cs = self.cs
-        r0, r1, t0, t1 = self.ranges[k]
-        loc, ins, out = self.locals[k]
         while True:
             self.start.wait()
             if self.stop:
                 return
-            if cs.lib.nano_compile(ctypes.byref(ins), ctypes.byref(out)) != 0:
-                raise RuntimeError("oracle rejected a range")
-            cs.outs["req"][t0:t1] += r0
-            cs.per["qsl"][r0 + 1:r1 + 1] = loc["qsl"][1:] + t0
-            cs.per["log"][r0:r1] = loc["log"][:r1 - r0] + t0
-            cs.scatter(t0, t1)
+            if k < self.compile_threads:
+                r0, r1, t0, t1 = self.ranges[k]
+                loc, ins, out = self.locals[k]
+                if cs.lib.nano_compile(ctypes.byref(ins), ctypes.byref(out)) != 0:
+                    raise RuntimeError("oracle rejected a range")
+                cs.outs["req"][t0:t1] += r0
+                cs.per["qsl"][r0 + 1:r1 + 1] = loc["qsl"][1:] + t0
+                cs.per["log"][r0:r1] = loc["log"][:r1 - r0] + t0
+            self.mid.wait()
+            a, b = self.tranges[k]
+            if b > a:
+                cs.scatter(a, b)
             self.done.wait()
 
     def step(self):
@@ -524,7 +534,10 @@ def cpu_baseline(w, seconds):
     want = {k: v.copy() for k, v in cs.outs.items()}
     want.update({k: v.copy() for k, v in cs.per.items()})
     want_disc = cs.disc.copy()
+    # the cores this process may use, at most the host share a thread pool
+    # should take (OMP_NUM_THREADS when set)
     allowed = len(os.sched_getaffinity(0))
+    allowed = max(1, min(allowed, int(os.environ.get("OMP_NUM_THREADS") or allowed)))
     one, n1 = _median_rate(cs.single, cs.N, seconds / 2)
     par = _CpuParallel(cs, allowed)
     for d in list(cs.outs.values()) + list(cs.per.values()):
@@ -548,10 +561,12 @@ def cpu_baseline(w, seconds):
                        f"{n1} steps in {seconds / 2:.0f} s; single-thread C oracle (nano-vllm block-range "
                        f"compile, memcpy K/V scatter into mmap'd full-size host caches, hidden-row gather)",
                 all_cores=dict(value=many, unit="tokens/s", cores=par.threads_used, pool=allowed,
+                               compile_threads=par.compile_threads,
                                sample=f"median of 5 blocks, {n2} steps in {seconds / 2:.0f} s; the same oracle "
-                                      f"on {par.threads_used} threads, one contiguous range of requests each "
-                                      f"(balanced by scheduled tokens; per-request parallelism, so never more "
-                                      f"threads than requests), K/V rows split the same way"))
+                                      f"on {par.threads_used} threads: the compile split into "
+                                      f"{par.compile_threads} contiguous ranges of requests (balanced by scheduled "
+                                      f"tokens; never more ranges than requests), then the K/V rows split into "
+                                      f"{par.threads_used} contiguous ranges of tokens"))
 
 
 def kv_sources_cached(ric, torch, sets, nbytes, reps=20):

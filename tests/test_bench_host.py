@@ -103,13 +103,17 @@ def test_library_path_rule():
 
 
 def test_cpu_baseline_parallel_equals_single(tmp_path):
-    """The all-cores CPU step (request ranges on threads, then the running
-    totals, compaction and padding) gives the single-thread oracle's outputs;
-    cpu_baseline itself asserts this before timing."""
+    """The all-cores CPU step (request ranges compiled on threads, K/V rows
+    split by tokens over every thread, then the running totals, compaction and
+    padding) gives the single-thread oracle's outputs; cpu_baseline itself
+    asserts this before timing."""
+    pool = len(os.sched_getaffinity(0))
     w = workloads.get("worked_example")
     res = bench.cpu_baseline(w, 0.2)
     assert res["kind"] == "oracle" and res["cores"] == 1 and res["value"] > 0
-    assert 1 <= res["all_cores"]["cores"] <= min(3, len(os.sched_getaffinity(0)))
+    assert 1 <= res["all_cores"]["compile_threads"] <= min(3, pool)
+    assert 1 <= res["all_cores"]["cores"] <= pool
     res = bench.cpu_baseline(workloads.get("mixed"), 0.5)
-    assert 1 <= res["all_cores"]["cores"] <= min(124, len(os.sched_getaffinity(0)))
+    assert 1 <= res["all_cores"]["compile_threads"] <= min(124, pool)
+    assert res["all_cores"]["cores"] >= res["all_cores"]["compile_threads"]
     assert res["all_cores"]["value"] > 0
