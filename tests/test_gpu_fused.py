@@ -214,6 +214,30 @@ def test_fused_empty_batch_is_all_padding(rt):
     b.close()
 
 
+@pytest.mark.parametrize("R", [255, 256, 257, 512])
+def test_fused_around_the_counters_first_limit(rt, R):
+    """With at most 256 requests each thread of a token workgroup loads its
+    own request's counters before the K/V rows; above that the counters are
+    loaded in a loop after them.  Batches of 255-512 requests (decodes and
+    short prefills, spare rows past R) through the single kernel: every
+    output and cache byte against the oracle."""
+    rng = np.random.default_rng(7000 + R)
+    B, M = 16, 256
+    pool = R * -(-M // B) + 1
+    reqs = workloads.random_batch(rng, num_reqs=R, block_size=B, max_model_len=M, num_kv_blocks=pool,
+                                  max_q=6, max_c=200)
+    N = sum(r.num_scheduled for r in reqs)
+    w = workloads.Workload("fused_counters", block_size=B, max_num_reqs=R + 7, max_model_len=M,
+                           max_blocks_per_req=-(-M // B), max_num_batched_tokens=N + 5, num_kv_blocks=pool,
+                           kv_heads=8, head_dim=128, kv_dtype="bf16", num_layers=2, hidden_size=64, gather="all",
+                           initial=reqs, capture_sizes=[N + 5], seed=R)
+    b, exp = _prepare(rt, w)
+    s, kv = _fused_step(rt, w, b, exp, 0x5A5A, flags=ALWAYS)
+    assert_step_equal(b.step_outputs(s), exp, f"{R} requests")
+    _check_all(w, exp, kv, 0x5A5A, f"{R} requests")
+    b.close()
+
+
 def test_fused_at_the_row_limit(rt):
     """8000 requests (the row limit: the largest prefix sum a workgroup keeps
     in LDS) through the single kernel, decodes and short prefills mixed."""
