@@ -626,9 +626,13 @@ bool fused_kv_supported(int row_bytes) { return row_bytes == 1024 || row_bytes =
 // Steps of long per-request runs (few requests: a short prefix sum) take two
 // rows per wave and load only the first before the prefix sum: loading every
 // row up front puts more reads in flight than some machines serve well
-// (long-context: 48 us against 52 us all-first, and 50 us for the compile and
-// the K/V kernel as two launches).  Other steps load every row first, so the
-// longer prefix sum over many requests hides behind them, with two rows per
+// (long-context, calls back to back: 48 us against 52 us all-first, and 50 us
+// for the compile and the K/V kernel as two launches; after other kernels the
+// shape takes 55-57 us, so the library's own choice gives such steps two
+// launches and this shape runs only when asked for).  Other steps load every
+// row first, so the longer prefix sum over many requests hides behind them
+// (with at most 256 requests the counters are loaded just before those
+// rows), with two rows per
 // wave when that still gives at least 2048 token workgroups over the layers
 // (eight per compute unit) and one otherwise (decode-heavy: 13.2 us with one
 // row per wave, 16.5 with four).
