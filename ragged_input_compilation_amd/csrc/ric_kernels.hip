@@ -632,10 +632,9 @@ bool fused_kv_supported(int row_bytes) { return row_bytes == 1024 || row_bytes =
 // launches and this shape runs only when asked for).  Other steps load every
 // row first, so the longer prefix sum over many requests hides behind them
 // (with at most 256 requests the counters are loaded just before those
-// rows), with two rows per
-// wave when that still gives at least 2048 token workgroups over the layers
-// (eight per compute unit) and one otherwise (decode-heavy: 13.2 us with one
-// row per wave, 16.5 with four).
+// rows), with two rows per wave when that still gives at least 2048 token
+// workgroups over the layers (eight per compute unit) and one otherwise
+// (decode-heavy: 13.2 us with one row per wave, 16.5 with four).
 template <int CPL>
 static void launch_fused(const CompileParams& p_in, const KVParams& kv, int num_layers, bool long_runs,
                          hipStream_t s) {
