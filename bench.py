@@ -841,10 +841,30 @@ def compile_kv_paths(torch, sets, sb, reps, cold_reps, flush_buf):
         gather = lambda st: st.gather()
         warm = bracketed(torch, sets, nothing, body, gather, reps)
         cold = bracketed(torch, sets, nothing, body, gather, cold_reps, flush_buf)
+        sustained = sustained_steps(torch, sets, flags)
         out[name] = {"warm_us": warm * 1e3, "warm_frac_of_peak": nbytes / (warm * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                      "after_cache_flush_us": cold * 1e3,
-                     "after_cache_flush_frac_of_peak": nbytes / (cold * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+                     "after_cache_flush_frac_of_peak": nbytes / (cold * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                     "sustained_step_us": sustained * 1e3}
     return out
+
+
+def sustained_steps(torch, sets, flags, steps=200):
+    """Wall-clock ms per step of `steps` back-to-back rotating steps (compile +
+    K/V through the given path, then the gather), bracketed by device
+    synchronisation: the steady rate, where per-call events can favour a
+    kernel that benefits from following itself."""
+    for i in range(10):
+        sets[i % len(sets)].compile_kv(flags)
+        sets[i % len(sets)].gather()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        st = sets[i % len(sets)]
+        st.compile_kv(flags)
+        st.gather()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
 
 
 def extra_config(ric, runner, torch, workloads, name, steps, warmup, with_next_rows=False):
