@@ -843,7 +843,7 @@ __global__ __launch_bounds__(256) void padded_table_kernel(PaddedTableParams p) 
     const int r = blockIdx.y;
     const int j = blockIdx.x * 256 + threadIdx.x;
     if (j >= p.width) return;
-    const int nb = min((int64_t)p.num_blocks[r], p.blk_stride);
+    const int nb = (int)min((int64_t)p.num_blocks[r], p.blk_stride);   // the stride fits an int
     // ratio > 1: each stored (manager) block id m stands for kernel blocks
     // m*ratio .. m*ratio + ratio-1 ([P1 §混合 KV Cache], map_to_kernel_blocks)
     const int b = j / p.ratio;

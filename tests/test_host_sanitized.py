@@ -291,7 +291,8 @@ def test_host_control_plane_under_asan_and_ubsan(tmp_path):
                     "-I", "/opt/rocm/include", "-I", os.path.join(ROOT, "include"),
                     os.path.join(ROOT, "ragged_input_compilation_amd", "csrc", "ric_host.cpp"),
                     os.path.join(ROOT, "tests", "host_fake", "fake_device.cpp"), "-o", str(so)], check=True)
-    env = {**os.environ, "LD_PRELOAD": asan, "ASAN_OPTIONS": "detect_leaks=0:abort_on_error=1",
+    preload = ":".join(x for x in (asan, os.environ.get("LD_PRELOAD", "")) if x)   # ASan first, nothing removed
+    env = {**os.environ, "LD_PRELOAD": preload, "ASAN_OPTIONS": "detect_leaks=0:abort_on_error=1",
            "RIC_LIBRARY": str(so)}
     child = subprocess.run([sys.executable, "-c", _CHILD.format(root=ROOT)], capture_output=True, text=True,
                            timeout=600, env=env)

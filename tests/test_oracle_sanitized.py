@@ -76,7 +76,8 @@ def _run_sanitized(src_text, tmp_path):
     so = tmp_path / "nano_oracle_sanitized.so"
     subprocess.run(["gcc", "-O1", "-g", "-std=c99", "-fPIC", "-shared", "-fsanitize=address,undefined",
                     "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", str(src), "-o", str(so)], check=True)
-    env = {**os.environ, "LD_PRELOAD": _asan_runtime(), "ASAN_OPTIONS": "detect_leaks=0:abort_on_error=1"}
+    preload = ":".join(x for x in (_asan_runtime(), os.environ.get("LD_PRELOAD", "")) if x)   # ASan first
+    env = {**os.environ, "LD_PRELOAD": preload, "ASAN_OPTIONS": "detect_leaks=0:abort_on_error=1"}
     return subprocess.run([sys.executable, "-c", _CHILD.format(root=ROOT, so=str(so))], capture_output=True,
                           text=True, timeout=300, env=env)
 
