@@ -375,18 +375,18 @@ int ric_compile(ric_batch* b, int32_t num_tokens_padded, ric_step* out);
  * mapping over all num_tokens_padded tokens, on the handle's stream, with
  * the same outputs and cache contents as those two calls
  * ([P1 §3. 物理 KV 槽位], [P3 §实现]: each token's K/V row goes to the slot the
- * compile gives it).  For rows of 1, 2 or 4 KiB the compile and the K/V write
- * of up to 32 layers are one kernel: each workgroup derives its own tokens'
- * slots and copies their rows, so there is no second launch to wait for.
- * flags picks the path: 0 lets the library choose (the single kernel,
- * except for steps whose scheduled tokens average 1024 or more per request:
- * those long contiguous runs go through the compile kernel and the K/V
- * kernel, which measured faster whenever other kernels ran just before),
- * RIC_FUSE_ALWAYS asks for the single kernel (with a tile shape of its own
- * for long runs, faster only in calls made back to back), RIC_FUSE_NEVER for
- * the two kernels; any
- * other bit is EINVAL.  Other row sizes and layers past 32 use
- * the separate K/V kernel after the compile.  The other
+ * compile gives it).  For rows of 256 B, 512 B, 1, 2 or 4 KiB the compile and
+ * the K/V write of up to 32 layers are one kernel: each workgroup derives its
+ * own tokens' slots and copies their rows, so there is no second launch to
+ * wait for.  flags picks the path: 0 lets the library choose (the single
+ * kernel, except for steps with rows of 1 KiB or more whose scheduled tokens
+ * average 1024 or more per request: those long contiguous runs go through
+ * the compile kernel and the K/V kernel, which measured faster whenever
+ * other kernels ran just before), RIC_FUSE_ALWAYS asks for the single kernel
+ * (with a tile shape of its own for such long runs, faster only in calls
+ * made back to back), RIC_FUSE_NEVER for the two kernels; any other bit is
+ * EINVAL.  Other row sizes and layers past 32 use the separate K/V kernel
+ * after the compile.  The other
  * K/V arguments are those of ric_reshape_and_cache (k, v, k_cache, v_cache:
  * host arrays of num_layers device pointers; src_row_stride 0 = row_bytes;
  * dev_status optional; num_slots the cache rows, a slot outside [0,

@@ -1233,15 +1233,20 @@ int ric_compile_and_cache(ric_batch* b, int32_t n_pad, const void* const* k, con
     const CompileParams p = compile_params(b, n_pad);
     kv.slot = b->d_slot;
     // A step whose scheduled tokens average 1024 or more per request is mostly
-    // long contiguous runs.  The library's own choice keeps those on the
-    // compile kernel followed by the K/V kernel's small streaming tiles: the
-    // single kernel's tile shape for them is faster only when it runs right
-    // after itself (long-context 46.7 against 50.3 us) and slower after any
-    // other kernel (55-57 us after a read, a matrix product or an idle gap,
-    // 70 us after a large write), while the two kernels take 51 us in every
-    // case.  Other steps take the single kernel.
+    // long contiguous runs.  With rows of 1 KiB or more the library's own
+    // choice keeps those on the compile kernel followed by the K/V kernel's
+    // small streaming tiles: the single kernel's tile shape for them is
+    // faster only when it runs right after itself (long-context 46.7 against
+    // 50.3 us) and slower after any other kernel (55-57 us after a read, a
+    // matrix product or an idle gap, 70 us after a large write), while the
+    // two kernels take 51 us in every case.  With narrower rows (a tensor-
+    // parallel shard's heads) the compile is a larger share of the step and
+    // the single kernel stays ahead after other kernels too (long-context,
+    // 256 B rows: 9.8 against 14.8 us after matrix products), so every step
+    // takes it; so do all other steps.
     const bool long_runs = (int64_t)b->sched_N >= (int64_t)1024 * std::max<int32_t>(b->sched_R, 1);
-    const bool fuse = (path == RIC_FUSE_ALWAYS || (path == 0 && !long_runs)) && num_layers > 0 && n_pad > 0 &&
+    const bool own_choice_fuses = !long_runs || row_bytes < 1024;
+    const bool fuse = (path == RIC_FUSE_ALWAYS || (path == 0 && own_choice_fuses)) && num_layers > 0 && n_pad > 0 &&
                       fused_kv_supported(row_bytes);
     int32_t done = 0;
     if (fuse) {

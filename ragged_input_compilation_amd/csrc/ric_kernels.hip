@@ -549,11 +549,14 @@ __device__ __forceinline__ int scan_own_counters(const CompileParams& p, const C
     return N;
 }
 
-template <int CPL, int ROWS, int PRE>
+template <int CPL, int ROWS, int PRE, int SUB>
 __global__ __launch_bounds__(kCompileThreads) void compile_kv_kernel(CompileParams p, KVParams kv) {
     static_assert(PRE >= 0 && PRE <= ROWS, "rows loaded early must be rows of the wave");
+    static_assert(SUB == 1 || CPL == 1, "rows narrower than 1 KiB take one 16-byte chunk per lane");
     constexpr int WAVES = kCompileThreads / kWave;
-    constexpr int TT = ROWS * WAVES;
+    constexpr int LPR = kWave / SUB;           // lanes per row: SUB rows share one wave load
+    constexpr int TW = ROWS * SUB;             // tokens per wave
+    constexpr int TT = TW * WAVES;
     extern __shared__ int32_t smem[];
     const CompileLds L(smem, p.num_reqs);
     int32_t* s_slot = smem + 2 * p.num_reqs + 1 + CompileLds::extra_words;   // [TT]
@@ -561,16 +564,18 @@ __global__ __launch_bounds__(kCompileThreads) void compile_kv_kernel(CompilePara
     const bool req_wg = (int)blockIdx.x >= p.num_token_tiles;
     if (req_wg && layer != 0) return;          // whole workgroup: before any barrier
     const int lane = threadIdx.x & (kWave - 1);
+    const int sub = lane / LPR;                // this lane's row within a wave load
+    const int64_t lane_off = (int64_t)(lane % LPR) * 16;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int tile0 = blockIdx.x * TT;
-    const int t0 = tile0 + wid * ROWS;         // this wave's first row
+    const int t0 = tile0 + wid * TW;           // this wave's first token
     const uint8_t* __restrict__ ks = kv.k[layer];
     const uint8_t* __restrict__ vs = kv.v[layer];
     u32x4 a[ROWS][2 * CPL];
     auto load_row = [&](int r) {
-        const int t = t0 + r;
+        const int t = t0 + r * SUB + sub;
         if (t < p.n_pad) {
-            const int64_t so = (int64_t)t * kv.src_stride + lane * 16;
+            const int64_t so = (int64_t)t * kv.src_stride + lane_off;
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
                 a[r][c] = load16<true>(ks + so + c * 1024);
@@ -603,27 +608,29 @@ __global__ __launch_bounds__(kCompileThreads) void compile_kv_kernel(CompilePara
     uint8_t* __restrict__ vd = kv.vc[layer];
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
-        const int t = t0 + r;
-        if (t >= p.n_pad) break;
-        const int s = s_slot[wid * ROWS + r];
+        const int t = t0 + r * SUB + sub;
+        if (t >= p.n_pad) continue;
+        const int s = s_slot[wid * TW + r * SUB + sub];
         if (s >= 0 && (int64_t)s < kv.num_slots) {
-            const int64_t off = (int64_t)s * kv.row_bytes + lane * 16;
+            const int64_t off = (int64_t)s * kv.row_bytes + lane_off;
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
                 store16<true>(kd + off + c * 1024, a[r][c]);
                 store16<true>(vd + off + c * 1024, a[r][CPL + c]);
             }
-        } else if (lane == 0 && kv.status != nullptr) {
+        } else if (lane % LPR == 0 && kv.status != nullptr) {
             atomicAdd(kv.status, 2);
         }
     }
 }
 
-bool fused_kv_supported(int row_bytes) { return row_bytes == 1024 || row_bytes == 2048 || row_bytes == 4096; }
+bool fused_kv_supported(int row_bytes) {
+    return row_bytes == 256 || row_bytes == 512 || row_bytes == 1024 || row_bytes == 2048 || row_bytes == 4096;
+}
 
-// Tile shape, from sweeps on MI355X over 1/2/4/8 rows per wave, rows loaded
-// before or after the prefix sum, other tile orders and a persistent grid.
-// Steps of long per-request runs (few requests: a short prefix sum) take two
+// Tile shape.  Rows of 1 KiB or more, from sweeps on MI355X over 1/2/4/8 rows
+// per wave, rows loaded before or after the prefix sum, other tile orders and
+// a persistent grid: steps of long per-request runs (few requests: a short prefix sum) take two
 // rows per wave and load only the first before the prefix sum: loading every
 // row up front puts more reads in flight than some machines serve well
 // (long-context, calls back to back: 48 us against 52 us all-first, and 50 us
@@ -635,27 +642,49 @@ bool fused_kv_supported(int row_bytes) { return row_bytes == 1024 || row_bytes =
 // rows), with two rows per wave when that still gives at least 2048 token
 // workgroups over the layers (eight per compute unit) and one otherwise
 // (decode-heavy: 13.2 us with one row per wave, 16.5 with four).
-template <int CPL>
+template <int CPL, int SUB>
 static void launch_fused(const CompileParams& p_in, const KVParams& kv, int num_layers, bool long_runs,
                          hipStream_t s) {
     CompileParams p = p_in;
     constexpr int WAVES = kCompileThreads / kWave;
-    const bool two = long_runs || (int64_t)((p.n_pad + 2 * WAVES - 1) / (2 * WAVES)) * num_layers >= 2048;
-    const int TT = (two ? 2 : 1) * WAVES;
+    int rows, pre;
+    if (SUB > 1) {
+        // Rows narrower than 1 KiB: a workgroup moves few bytes per token, so
+        // its prefix sum weighs more; every row is loaded first, two rows per
+        // wave, four above 256 requests (churn's 1024: 15.3 against 16.4 us
+        // with two, 512 B rows), long runs included.
+        rows = p.num_reqs > kCompileThreads ? 4 : 2;
+        pre = rows;
+    } else {
+        const bool two = long_runs || (int64_t)((p.n_pad + 2 * WAVES - 1) / (2 * WAVES)) * num_layers >= 2048;
+        rows = two ? 2 : 1;
+        pre = long_runs ? 1 : rows;
+    }
+    const int TT = rows * SUB * WAVES;
     p.num_token_tiles = (p.n_pad + TT - 1) / TT;
     const dim3 grid(p.num_token_tiles + 1, num_layers);
     const size_t lds = compile_lds_bytes(p.num_reqs, TT);
-    if (long_runs) hipLaunchKernelGGL((compile_kv_kernel<CPL, 2, 1>), grid, dim3(kCompileThreads), lds, s, p, kv);
-    else if (two) hipLaunchKernelGGL((compile_kv_kernel<CPL, 2, 2>), grid, dim3(kCompileThreads), lds, s, p, kv);
-    else hipLaunchKernelGGL((compile_kv_kernel<CPL, 1, 1>), grid, dim3(kCompileThreads), lds, s, p, kv);
+    const dim3 block(kCompileThreads);
+    if constexpr (SUB > 1) {
+        if (rows == 4) hipLaunchKernelGGL((compile_kv_kernel<CPL, 4, 4, SUB>), grid, block, lds, s, p, kv);
+        else hipLaunchKernelGGL((compile_kv_kernel<CPL, 2, 2, SUB>), grid, block, lds, s, p, kv);
+    } else {
+        if (pre == 1 && rows == 2) hipLaunchKernelGGL((compile_kv_kernel<CPL, 2, 1, 1>), grid, block, lds, s, p, kv);
+        else if (rows == 2) hipLaunchKernelGGL((compile_kv_kernel<CPL, 2, 2, 1>), grid, block, lds, s, p, kv);
+        else hipLaunchKernelGGL((compile_kv_kernel<CPL, 1, 1, 1>), grid, block, lds, s, p, kv);
+    }
 }
 
 hipError_t launch_compile_kv(const CompileParams& p, const KVParams& kv, int num_layers, bool long_runs,
                              hipStream_t s) {
     if (num_layers < 1 || !fused_kv_supported(kv.row_bytes)) return hipErrorInvalidValue;
-    if (kv.row_bytes == 1024) launch_fused<1>(p, kv, num_layers, long_runs, s);
-    else if (kv.row_bytes == 2048) launch_fused<2>(p, kv, num_layers, long_runs, s);
-    else launch_fused<4>(p, kv, num_layers, long_runs, s);
+    switch (kv.row_bytes) {
+    case 256: launch_fused<1, 4>(p, kv, num_layers, long_runs, s); break;
+    case 512: launch_fused<1, 2>(p, kv, num_layers, long_runs, s); break;
+    case 1024: launch_fused<1, 1>(p, kv, num_layers, long_runs, s); break;
+    case 2048: launch_fused<2, 1>(p, kv, num_layers, long_runs, s); break;
+    default: launch_fused<4, 1>(p, kv, num_layers, long_runs, s); break;
+    }
     return hipGetLastError();
 }
 

@@ -91,15 +91,21 @@ def test_more_than_one_gpu_is_refused(gpus):
 
 
 def test_library_path_rule():
-    """The bench's mirror of the library's choice: one kernel for 1/2/4 KiB
-    rows unless the step averages 1024 or more tokens per request."""
-    for name in ("churn", "mixed", "decode_heavy"):
+    """The bench's mirror of the library's choice: one kernel for rows of
+    256 B and 512 B, and for 1/2/4 KiB rows unless the step averages 1024 or
+    more tokens per request; other row sizes take two kernels."""
+    import dataclasses
+    for name in ("churn", "mixed", "decode_heavy", "worked_example"):     # the last: 256 B rows
         assert bench.fused_path(workloads.get(name)), name
-    assert not bench.fused_path(workloads.get("long_context"))
-    assert not bench.fused_path(workloads.get("worked_example"))      # 256 B rows
+    lc = workloads.get("long_context")
+    assert not bench.fused_path(lc)
+    assert bench.fused_path(dataclasses.replace(lc, kv_heads=1))        # 256 B rows: long runs too
+    assert bench.fused_path(dataclasses.replace(lc, kv_heads=2))
+    assert not bench.fused_path(dataclasses.replace(workloads.get("mixed"), kv_heads=12))   # 3 KiB rows
+    assert not bench.fused_path(dataclasses.replace(workloads.get("worked_example"), kv_heads=1))   # 128 B
     assert bench.dominant_kernel(workloads.get("churn"), 16384) == "compile_kv_kernel"
-    assert bench.dominant_kernel(workloads.get("long_context"), 32768) == "kv_chunk_kernel"
-    assert bench.dominant_kernel(workloads.get("worked_example"), 32) == "kv_chunk_kernel"
+    assert bench.dominant_kernel(lc, 32768) == "kv_chunk_kernel"
+    assert bench.dominant_kernel(workloads.get("worked_example"), 32) == "compile_kv_kernel"
 
 
 def test_cpu_baseline_parallel_equals_single(tmp_path):

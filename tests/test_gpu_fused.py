@@ -101,13 +101,13 @@ def _random_workload(rng, trial, head_choices):
 
 
 def test_fused_random_batches(rt):
-    """Sixty seeded batches: block sizes 1 to 64 (shift and division paths),
-    decode-only to 300-token chunks, up to 300 requests, padded tails of up to
-    69 tokens, 1-3 layers, rows of 1, 2 and 4 KiB (fused) and 256 B and 3 KiB
-    (compile, then the separate K/V kernel)."""
+    """Seventy seeded batches: block sizes 1 to 64 (shift and division
+    paths), decode-only to 300-token chunks, up to 300 requests, padded tails
+    of up to 69 tokens, 1-3 layers, rows of 256 B, 512 B, 1, 2 and 4 KiB
+    (fused) and 128 B and 3 KiB (compile, then the separate K/V kernel)."""
     rng = np.random.default_rng(4321)
-    heads = [(4, 128), (8, 128), (16, 128), (1, 128), (12, 128)]
-    for trial in range(60):
+    heads = [(4, 128), (8, 128), (16, 128), (1, 128), (12, 128), (2, 128), (1, 64)]
+    for trial in range(70):
         w = _random_workload(rng, trial, heads)
         label = f"trial {trial}: B={w.block_size} R={len(w.initial)} row={w.row_bytes} L={w.num_layers}"
         b, exp = _prepare(rt, w)
@@ -214,13 +214,14 @@ def test_fused_empty_batch_is_all_padding(rt):
     b.close()
 
 
-@pytest.mark.parametrize("R", [255, 256, 257, 512])
-def test_fused_around_the_counters_first_limit(rt, R):
+@pytest.mark.parametrize("R,heads", [(255, 8), (256, 8), (257, 8), (512, 8), (256, 1), (257, 1), (512, 2)])
+def test_fused_around_the_counters_first_limit(rt, R, heads):
     """With at most 256 requests each thread of a token workgroup loads its
     own request's counters before the K/V rows; above that the counters are
-    loaded in a loop after them.  Batches of 255-512 requests (decodes and
-    short prefills, spare rows past R) through the single kernel: every
-    output and cache byte against the oracle."""
+    loaded in a loop after them (and rows narrower than 1 KiB take four rows
+    per wave instead of two).  Batches of 255-512 requests (decodes and short
+    prefills, spare rows past R) through the single kernel, rows of 2 KiB,
+    256 B and 512 B: every output and cache byte against the oracle."""
     rng = np.random.default_rng(7000 + R)
     B, M = 16, 256
     pool = R * -(-M // B) + 1
@@ -229,12 +230,12 @@ def test_fused_around_the_counters_first_limit(rt, R):
     N = sum(r.num_scheduled for r in reqs)
     w = workloads.Workload("fused_counters", block_size=B, max_num_reqs=R + 7, max_model_len=M,
                            max_blocks_per_req=-(-M // B), max_num_batched_tokens=N + 5, num_kv_blocks=pool,
-                           kv_heads=8, head_dim=128, kv_dtype="bf16", num_layers=2, hidden_size=64, gather="all",
-                           initial=reqs, capture_sizes=[N + 5], seed=R)
+                           kv_heads=heads, head_dim=128, kv_dtype="bf16", num_layers=2, hidden_size=64,
+                           gather="all", initial=reqs, capture_sizes=[N + 5], seed=R)
     b, exp = _prepare(rt, w)
     s, kv = _fused_step(rt, w, b, exp, 0x5A5A, flags=ALWAYS)
-    assert_step_equal(b.step_outputs(s), exp, f"{R} requests")
-    _check_all(w, exp, kv, 0x5A5A, f"{R} requests")
+    assert_step_equal(b.step_outputs(s), exp, f"{R} requests, {w.row_bytes} B rows")
+    _check_all(w, exp, kv, 0x5A5A, f"{R} requests, {w.row_bytes} B rows")
     b.close()
 
 
@@ -261,8 +262,10 @@ def test_fused_long_runs(rt):
     request on average), alternately through the single kernel's long-run
     tile shape and the library's own choice (two kernels), 24 seeded
     batches: 1-8 requests, chunks of 1024-4096 tokens on cached prefixes up to
-    4000, block sizes 1, 16, 64 and 100, rows of 1, 2 and 4 KiB, 1-3 layers,
-    padded tails; every output and cache byte against the oracle."""
+    4000, block sizes 1, 16, 64 and 100, rows of 256 B, 512 B, 1, 2 and 4
+    KiB (the narrow ones take the single kernel by the library's own choice
+    too), 1-3 layers, padded tails; every output and cache byte against the
+    oracle."""
     rng = np.random.default_rng(1024)
     for trial in range(24):
         B = int(rng.choice([1, 16, 64, 100]))
@@ -274,7 +277,7 @@ def test_fused_long_runs(rt):
         N = sum(r.num_scheduled for r in reqs)
         if N < 1024 * R:                    # not a long-run step: drawn again in the next trial
             continue
-        heads = (4, 8, 16)[trial % 3]
+        heads = (4, 8, 16, 1, 2)[trial % 5]
         n_pad = N + int(rng.integers(0, 40))
         w = workloads.Workload("long_runs", block_size=B, max_num_reqs=R + 2, max_model_len=M,
                                max_blocks_per_req=-(-M // B), max_num_batched_tokens=n_pad, num_kv_blocks=pool,
