@@ -27,7 +27,7 @@ enum ScalarCol : int {
 constexpr int kMaxGroups = 4;             // KV-cache groups per handle
 __host__ __device__ inline int blocks_col(int g) { return g == 0 ? kNumBlocks : kNumBlocksG1 + g - 1; }
 
-constexpr int kMaxReqsLimit = 8000;       // compile LDS: (2R + 21) int32 per workgroup < 64 KiB
+constexpr int kMaxReqsLimit = 8000;       // compile LDS: 2R + 21 int32 (+ up to 128 slots) < 64 KiB
 constexpr int kMaxLayersPerLaunch = 32;   // K/V pointer sets passed by value
 constexpr int kNumDevScalars = 8;
 

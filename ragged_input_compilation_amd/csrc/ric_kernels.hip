@@ -625,7 +625,8 @@ __global__ __launch_bounds__(kCompileThreads) void compile_kv_kernel(CompilePara
 }
 
 bool fused_kv_supported(int row_bytes) {
-    return row_bytes == 256 || row_bytes == 512 || row_bytes == 1024 || row_bytes == 2048 || row_bytes == 4096;
+    return row_bytes == 128 || row_bytes == 256 || row_bytes == 512 || row_bytes == 1024 || row_bytes == 2048 ||
+           row_bytes == 4096;
 }
 
 // Tile shape.  Rows of 1 KiB or more, from sweeps on MI355X over 1/2/4/8 rows
@@ -679,6 +680,7 @@ hipError_t launch_compile_kv(const CompileParams& p, const KVParams& kv, int num
                              hipStream_t s) {
     if (num_layers < 1 || !fused_kv_supported(kv.row_bytes)) return hipErrorInvalidValue;
     switch (kv.row_bytes) {
+    case 128: launch_fused<1, 8>(p, kv, num_layers, long_runs, s); break;
     case 256: launch_fused<1, 4>(p, kv, num_layers, long_runs, s); break;
     case 512: launch_fused<1, 2>(p, kv, num_layers, long_runs, s); break;
     case 1024: launch_fused<1, 1>(p, kv, num_layers, long_runs, s); break;

@@ -102,7 +102,8 @@ def test_library_path_rule():
     assert bench.fused_path(dataclasses.replace(lc, kv_heads=1))        # 256 B rows: long runs too
     assert bench.fused_path(dataclasses.replace(lc, kv_heads=2))
     assert not bench.fused_path(dataclasses.replace(workloads.get("mixed"), kv_heads=12))   # 3 KiB rows
-    assert not bench.fused_path(dataclasses.replace(workloads.get("worked_example"), kv_heads=1))   # 128 B
+    assert bench.fused_path(dataclasses.replace(workloads.get("worked_example"), kv_heads=1))       # 128 B
+    assert not bench.fused_path(dataclasses.replace(workloads.get("worked_example"), kv_heads=1, head_dim=32))
     assert bench.dominant_kernel(workloads.get("churn"), 16384) == "compile_kv_kernel"
     assert bench.dominant_kernel(lc, 32768) == "kv_chunk_kernel"
     assert bench.dominant_kernel(workloads.get("worked_example"), 32) == "compile_kv_kernel"

@@ -101,13 +101,13 @@ def _random_workload(rng, trial, head_choices):
 
 
 def test_fused_random_batches(rt):
-    """Seventy seeded batches: block sizes 1 to 64 (shift and division
+    """Eighty seeded batches: block sizes 1 to 64 (shift and division
     paths), decode-only to 300-token chunks, up to 300 requests, padded tails
-    of up to 69 tokens, 1-3 layers, rows of 256 B, 512 B, 1, 2 and 4 KiB
-    (fused) and 128 B and 3 KiB (compile, then the separate K/V kernel)."""
+    of up to 69 tokens, 1-3 layers, rows of 128 B, 256 B, 512 B, 1, 2 and 4
+    KiB (fused) and 64 B and 3 KiB (compile, then the separate K/V kernel)."""
     rng = np.random.default_rng(4321)
-    heads = [(4, 128), (8, 128), (16, 128), (1, 128), (12, 128), (2, 128), (1, 64)]
-    for trial in range(70):
+    heads = [(4, 128), (8, 128), (16, 128), (1, 128), (12, 128), (2, 128), (1, 64), (1, 32)]
+    for trial in range(80):
         w = _random_workload(rng, trial, heads)
         label = f"trial {trial}: B={w.block_size} R={len(w.initial)} row={w.row_bytes} L={w.num_layers}"
         b, exp = _prepare(rt, w)
@@ -214,14 +214,16 @@ def test_fused_empty_batch_is_all_padding(rt):
     b.close()
 
 
-@pytest.mark.parametrize("R,heads", [(255, 8), (256, 8), (257, 8), (512, 8), (256, 1), (257, 1), (512, 2)])
+@pytest.mark.parametrize("R,heads", [(255, 8), (256, 8), (257, 8), (512, 8), (256, 1), (257, 1), (512, 2),
+                                     (300, 0)])
 def test_fused_around_the_counters_first_limit(rt, R, heads):
     """With at most 256 requests each thread of a token workgroup loads its
     own request's counters before the K/V rows; above that the counters are
     loaded in a loop after them (and rows narrower than 1 KiB take four rows
     per wave instead of two).  Batches of 255-512 requests (decodes and short
     prefills, spare rows past R) through the single kernel, rows of 2 KiB,
-    256 B and 512 B: every output and cache byte against the oracle."""
+    128 B (heads 0: one head of 64), 256 B and 512 B: every output and cache
+    byte against the oracle."""
     rng = np.random.default_rng(7000 + R)
     B, M = 16, 256
     pool = R * -(-M // B) + 1
@@ -230,7 +232,8 @@ def test_fused_around_the_counters_first_limit(rt, R, heads):
     N = sum(r.num_scheduled for r in reqs)
     w = workloads.Workload("fused_counters", block_size=B, max_num_reqs=R + 7, max_model_len=M,
                            max_blocks_per_req=-(-M // B), max_num_batched_tokens=N + 5, num_kv_blocks=pool,
-                           kv_heads=heads, head_dim=128, kv_dtype="bf16", num_layers=2, hidden_size=64,
+                           kv_heads=max(heads, 1), head_dim=128 if heads else 64, kv_dtype="bf16", num_layers=2,
+                           hidden_size=64,
                            gather="all", initial=reqs, capture_sizes=[N + 5], seed=R)
     b, exp = _prepare(rt, w)
     s, kv = _fused_step(rt, w, b, exp, 0x5A5A, flags=ALWAYS)
