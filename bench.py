@@ -101,13 +101,13 @@ def kv_kernel_name(w, n_tokens):
 def fused_path(w):
     """Whether ric_compile_and_cache takes the single kernel for this step by
     the library's own choice (mirrors its rule: rows of 128, 256 or 512 B, or
-    rows of 1, 2 or 4 KiB with fewer than 1024 scheduled tokens per request
+    rows of 1, 2, 3, 4, 6 or 8 KiB with fewer than 1024 scheduled tokens per request
     on average)."""
     live = w.live_requests()
     N = sum(r.num_scheduled for r in live)
     if w.row_bytes in (128, 256, 512):
         return True
-    return w.row_bytes in (1024, 2048, 4096) and N < 1024 * max(len(live), 1)
+    return w.row_bytes in (1024, 2048, 3072, 4096, 6144, 8192) and N < 1024 * max(len(live), 1)
 
 
 def dominant_kernel(w, n_pad):

@@ -375,7 +375,7 @@ int ric_compile(ric_batch* b, int32_t num_tokens_padded, ric_step* out);
  * mapping over all num_tokens_padded tokens, on the handle's stream, with
  * the same outputs and cache contents as those two calls
  * ([P1 §3. 物理 KV 槽位], [P3 §实现]: each token's K/V row goes to the slot the
- * compile gives it).  For rows of 128 B, 256 B, 512 B, 1, 2 or 4 KiB the compile and
+ * compile gives it).  For rows of 128 B, 256 B, 512 B, 1, 2, 3, 4, 6 or 8 KiB the compile and
  * the K/V write of up to 32 layers are one kernel: each workgroup derives its
  * own tokens' slots and copies their rows, so there is no second launch to
  * wait for.  flags picks the path: 0 lets the library choose (the single

@@ -625,8 +625,10 @@ __global__ __launch_bounds__(kCompileThreads) void compile_kv_kernel(CompilePara
 }
 
 bool fused_kv_supported(int row_bytes) {
-    return row_bytes == 128 || row_bytes == 256 || row_bytes == 512 || row_bytes == 1024 || row_bytes == 2048 ||
-           row_bytes == 4096;
+    switch (row_bytes) {
+    case 128: case 256: case 512: case 1024: case 2048: case 3072: case 4096: case 6144: case 8192: return true;
+    default: return false;
+    }
 }
 
 // Tile shape.  Rows of 1 KiB or more, from sweeps on MI355X over 1/2/4/8 rows
@@ -685,7 +687,10 @@ hipError_t launch_compile_kv(const CompileParams& p, const KVParams& kv, int num
     case 512: launch_fused<1, 2>(p, kv, num_layers, long_runs, s); break;
     case 1024: launch_fused<1, 1>(p, kv, num_layers, long_runs, s); break;
     case 2048: launch_fused<2, 1>(p, kv, num_layers, long_runs, s); break;
-    default: launch_fused<4, 1>(p, kv, num_layers, long_runs, s); break;
+    case 3072: launch_fused<3, 1>(p, kv, num_layers, long_runs, s); break;
+    case 4096: launch_fused<4, 1>(p, kv, num_layers, long_runs, s); break;
+    case 6144: launch_fused<6, 1>(p, kv, num_layers, long_runs, s); break;
+    default: launch_fused<8, 1>(p, kv, num_layers, long_runs, s); break;
     }
     return hipGetLastError();
 }

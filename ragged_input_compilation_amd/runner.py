@@ -232,7 +232,7 @@ def reshape_and_cache(kv: KVSet, slot_mapping: int, num_tokens: int, dev_status:
 
 def compile_and_cache(batch: "Batch", n_pad: int, kv: KVSet, dev_status: int = 0, flags: int = 0) -> ric.ric_step:
     """Compile plus the K/V write of every layer in one library call (one
-    kernel for rows of 128 B to 4 KiB, unless the rows are 1 KiB or more and
+    kernel for rows of 128 B to 8 KiB, unless the rows are 1 KiB or more and
     the step is mostly long chunks; flags RIC_FUSE_ALWAYS / RIC_FUSE_NEVER
     force the path)."""
     return ric.ric_compile_and_cache(batch.h, n_pad, [t.data_ptr() for t in kv.k], [t.data_ptr() for t in kv.v],

@@ -174,8 +174,10 @@ hipError_t check_scratch_for_current_device(uint32_t** out) {
 
 hipError_t launch_compile(const CompileParams&, hipStream_t) { return hipSuccess; }
 bool fused_kv_supported(int row_bytes) {
-    return row_bytes == 128 || row_bytes == 256 || row_bytes == 512 || row_bytes == 1024 || row_bytes == 2048 ||
-           row_bytes == 4096;
+    switch (row_bytes) {
+    case 128: case 256: case 512: case 1024: case 2048: case 3072: case 4096: case 6144: case 8192: return true;
+    default: return false;
+    }
 }
 hipError_t launch_compile_kv(const CompileParams&, const KVParams&, int, bool, hipStream_t) { return hipSuccess; }
 hipError_t launch_kv_scatter(const KVParams&, int, hipStream_t) { return hipSuccess; }

@@ -92,8 +92,9 @@ def test_more_than_one_gpu_is_refused(gpus):
 
 def test_library_path_rule():
     """The bench's mirror of the library's choice: one kernel for rows of
-    256 B and 512 B, and for 1/2/4 KiB rows unless the step averages 1024 or
-    more tokens per request; other row sizes take two kernels."""
+    128, 256 and 512 B, and for rows of 1, 2, 3, 4, 6 and 8 KiB unless the
+    step averages 1024 or more tokens per request; other row sizes take two
+    kernels."""
     import dataclasses
     for name in ("churn", "mixed", "decode_heavy", "worked_example"):     # the last: 256 B rows
         assert bench.fused_path(workloads.get(name)), name
@@ -101,7 +102,9 @@ def test_library_path_rule():
     assert not bench.fused_path(lc)
     assert bench.fused_path(dataclasses.replace(lc, kv_heads=1))        # 256 B rows: long runs too
     assert bench.fused_path(dataclasses.replace(lc, kv_heads=2))
-    assert not bench.fused_path(dataclasses.replace(workloads.get("mixed"), kv_heads=12))   # 3 KiB rows
+    assert bench.fused_path(dataclasses.replace(workloads.get("mixed"), kv_heads=12))       # 3 KiB rows
+    assert not bench.fused_path(dataclasses.replace(lc, kv_heads=32))                       # 8 KiB long runs
+    assert not bench.fused_path(dataclasses.replace(workloads.get("mixed"), kv_heads=6))    # 1.5 KiB rows
     assert bench.fused_path(dataclasses.replace(workloads.get("worked_example"), kv_heads=1))       # 128 B
     assert not bench.fused_path(dataclasses.replace(workloads.get("worked_example"), kv_heads=1, head_dim=32))
     assert bench.dominant_kernel(workloads.get("churn"), 16384) == "compile_kv_kernel"

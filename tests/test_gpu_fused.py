@@ -103,10 +103,11 @@ def _random_workload(rng, trial, head_choices):
 def test_fused_random_batches(rt):
     """Eighty seeded batches: block sizes 1 to 64 (shift and division
     paths), decode-only to 300-token chunks, up to 300 requests, padded tails
-    of up to 69 tokens, 1-3 layers, rows of 128 B, 256 B, 512 B, 1, 2 and 4
-    KiB (fused) and 64 B and 3 KiB (compile, then the separate K/V kernel)."""
+    of up to 69 tokens, 1-3 layers, rows of 128 B, 256 B, 512 B, 1, 2, 3, 4
+    and 8 KiB (fused) and 64 B and 1.5 KiB (compile, then the separate K/V
+    kernel)."""
     rng = np.random.default_rng(4321)
-    heads = [(4, 128), (8, 128), (16, 128), (1, 128), (12, 128), (2, 128), (1, 64), (1, 32)]
+    heads = [(4, 128), (8, 128), (16, 128), (1, 128), (12, 128), (2, 128), (1, 64), (1, 32), (32, 128), (6, 128)]
     for trial in range(80):
         w = _random_workload(rng, trial, heads)
         label = f"trial {trial}: B={w.block_size} R={len(w.initial)} row={w.row_bytes} L={w.num_layers}"
