@@ -243,6 +243,37 @@ def test_fused_around_the_counters_first_limit(rt, R, heads):
     b.close()
 
 
+@pytest.mark.parametrize("heads", [1, 4, 8])
+def test_fused_strided_sources(rt, heads):
+    """K and V as views into one fused [N_pad, 3, H, D] projection output (row
+    stride three rows), rows of 256 B, 1 KiB and 2 KiB, through the single
+    kernel: every output and cache byte against the oracle."""
+    ric, runner = rt
+    rng = np.random.default_rng(3 + heads)
+    reqs = workloads.random_batch(rng, num_reqs=40, block_size=16, max_model_len=512, num_kv_blocks=40 * 33 + 1,
+                                  max_q=40, max_c=400)
+    N = sum(r.num_scheduled for r in reqs)
+    w = workloads.Workload("fused_strided", block_size=16, max_num_reqs=48, max_model_len=512,
+                           max_blocks_per_req=32, max_num_batched_tokens=N + 9, num_kv_blocks=40 * 33 + 1,
+                           kv_heads=heads, head_dim=128, kv_dtype="bf16", num_layers=2, hidden_size=64, gather="all",
+                           initial=reqs, capture_sizes=[N + 9], seed=heads)
+    b, exp = _prepare(rt, w)
+    n_pad = exp["n_pad"]
+    sentinel = 0x6E6E
+    kc, vc = runner.alloc_caches(w, fill=sentinel)
+    qkv = [torch.randn((n_pad, 3, heads, 128), device="cuda").to(torch.bfloat16) for _ in range(2)]
+    k = [t[:, 1] for t in qkv]
+    v = [t[:, 2] for t in qkv]
+    assert k[0].stride(0) == 3 * heads * 128
+    kv = runner.KVSet(k, v, kc, vc, w.row_bytes, w.num_kv_blocks * w.block_size)
+    s = runner.compile_and_cache(b, n_pad, kv, flags=ALWAYS)
+    torch.cuda.synchronize()
+    assert_step_equal(b.step_outputs(s), exp, f"strided {w.row_bytes} B")
+    _check_all(w, exp, runner.KVSet([t.contiguous() for t in k], [t.contiguous() for t in v], kc, vc, w.row_bytes,
+                                    kv.num_slots), sentinel, f"strided {w.row_bytes} B")
+    b.close()
+
+
 def test_fused_at_the_row_limit(rt):
     """8000 requests (the row limit: the largest prefix sum a workgroup keeps
     in LDS) through the single kernel, decodes and short prefills mixed."""
