@@ -82,6 +82,29 @@ def test_fused_step_matches_oracle(rt, name, flags):
     b.close()
 
 
+NARROW = [("long_context", 1), ("churn", 2), ("decode_heavy", 1), ("mixed", 2)]
+
+
+@pytest.mark.parametrize("name,heads", NARROW, ids=[f"{n}-{h * 256}B" for n, h in NARROW])
+def test_fused_full_size_narrow_rows(rt, name, heads):
+    """The configurations at full size with a tensor-parallel rank's rows
+    (one or two heads of 128: 256 B or 512 B) through the library's own
+    choice, which is the single kernel for these rows, long runs included:
+    every compile output, and every row of every K/V cache against the
+    oracle (real rows against their sources, all others still the
+    sentinel)."""
+    import dataclasses
+    w = dataclasses.replace(workloads.get(name), kv_heads=heads)
+    b, exp = _prepare(rt, w)
+    sentinel = 0x4B4B
+    s, kv = _fused_step(rt, w, b, exp, sentinel, flags=0)
+    assert_step_equal(b.step_outputs(s), exp, f"{name} {w.row_bytes} B")
+    _check_all(w, exp, kv, sentinel, f"{name} {w.row_bytes} B")
+    del kv
+    torch.cuda.empty_cache()
+    b.close()
+
+
 def _random_workload(rng, trial, head_choices):
     B = int(rng.choice([1, 2, 3, 4, 8, 16, 32, 64]))
     R = int(rng.integers(1, 300))
