@@ -887,6 +887,12 @@ def extra_config(ric, runner, torch, workloads, name, steps, warmup, with_next_r
            "step_bytes": sb["total"], "library_path": path, "compile_plus_kv": ck,
            "dominant_kernel": kernel, "dominant_kernel_traffic": load_traffic(kernel, name),
            "rotation_instances": len(sets), "seconds": None}
+    if sets[0].gather_rows:
+        # the gather alone (events around it, rotating instances): M rows of
+        # hidden states read and written, plus the M indices
+        ga = bracketed(torch, sets, lambda st: None, lambda st: st.gather(), lambda st: None, 30) * 1e3
+        gb = sb["gather"]
+        res["gather"] = {"rows": sets[0].gather_rows, "us": ga, "bytes": gb, "gbps": gb / (ga * 1e-6) / 1e9}
     if with_next_rows and name != "worked_example":
         res["next_rows"] = next_rows(ric, runner, torch, w0, sets[0])
     release(torch, sets)
