@@ -9,10 +9,11 @@
 // The device holds the column store; the host keeps only what validation and
 // row bookkeeping need (row <-> request maps and the per-row scalar columns).
 // Token and block payloads never live on the host beyond the pinned staging:
-// each mutation appends its payload to a pinned log, and a flush uploads the
-// whole log with one copy and scatters it with one kernel, instead of one
+// each mutation appends its payload to a pinned log, and a flush scatters the
+// whole log with one kernel (which reads a small log in place from the pinned
+// memory and a large one after one copy into device staging), instead of one
 // small copy per request.  Two pinned logs alternate, each guarded by an event
-// so the host never overwrites a log that a copy may still be reading
+// so the host never overwrites a log that the device may still be reading
 // ([P1 §为什么 CPU 侧同时要 tensor 和 NumPy view]: producer/consumer ordering
 // of pinned buffers).
 #include <hip/hip_runtime.h>
@@ -324,10 +325,10 @@ int stage(ric_batch* b, void* dst, const void* src, size_t n) {
     return RIC_OK;
 }
 
-// A graph captured during an upload would record the copy from a pinned log
-// that later flushes rewrite, and an apply kernel whose op count and offsets
-// belong to that one flush: a replay would scatter whatever the log then
-// holds.  Uploads therefore happen outside capture only; calls that stage and
+// A graph captured during an upload would record a read of a pinned log that
+// later flushes rewrite (in place, or through a copy), and an apply kernel
+// whose op count and offsets belong to that one flush: a replay would scatter
+// whatever the log then holds.  Uploads therefore happen outside capture only; calls that stage and
 // upload in one go check this before they stage anything.
 int refuse_if_capturing(ric_batch* b) {
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
@@ -526,8 +527,8 @@ int ric_create(const ric_config* cfg, void* stream, void* workspace, size_t work
         if (hipHostGetDevicePointer(&dp, p, 0) != hipSuccess)
             return bail(fail(RIC_EHIP, "pinned staging has no device address"));
         b->d_log[i] = static_cast<uint8_t*>(dp);
-        // These events only tell the host when a log's upload has finished
-        // reading it; no device write needs to become visible to the host, so
+        // These events only tell the host when the device has finished
+        // reading a log; no device write needs to become visible to the host, so
         // they skip the system-scope fence (an L2 write-back and invalidate
         // on every flush otherwise).
         if (hipEventCreateWithFlags(&b->ev[i], hipEventDisableTiming | hipEventDisableSystemFence) != hipSuccess)
