@@ -21,11 +21,12 @@ def rt():
     return _ric, runner
 
 
-@pytest.mark.parametrize("name,single", [("worked_example", False), ("mixed", False), ("mixed", True),
-                                         ("decode_heavy", True)])
+@pytest.mark.parametrize("name,single", [("worked_example", False), ("worked_example", True), ("mixed", False),
+                                         ("mixed", True), ("decode_heavy", True)])
 def test_captured_step_replays_match_eager(rt, name, single):
-    """`single`: the step is ric_compile_and_cache (one kernel for these rows)
-    + gather instead of three calls."""
+    """`single`: the step is ric_compile_and_cache (one kernel for these rows:
+    256 B in the worked example, 2 KiB otherwise) + gather instead of three
+    calls."""
     ric, runner = rt
     w = workloads.get(name)
     side = torch.cuda.Stream()
