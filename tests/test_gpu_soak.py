@@ -4,7 +4,7 @@ replaced block rows, condense, decode appends, prefill chunks, a second
 KV-cache group with its own block size, device-side appends of sampled
 tokens, history truncation, device-side corrections of computed counts (some
 with out-of-range accepted counts), and K/V writes, some of them through the
-single compile + K/V kernel (ric_compile_and_cache).  Every step's compile
+single compile + K/V kernel (ric_compile_and_cache, rows of 1 KiB and 256 B).  Every step's compile
 (group 1's slots included), every corrected count and every written cache row
 equals the oracle's."""
 import numpy as np
@@ -20,7 +20,7 @@ MR, M = 24, 256
 POOL = 20000
 BUDGET = 192
 ROW = 64
-ROWF = 1024          # rows the single compile + K/V kernel takes
+ROWF = (1024, 256)   # rows the single compile + K/V kernel takes (a wide and a narrow size)
 
 
 @pytest.fixture(scope="module")
@@ -47,10 +47,10 @@ def test_serving_loop_soak(rt):
     cache = torch.zeros((POOL * B0, ROW), dtype=torch.uint8, device="cuda")
     cache_ref = np.zeros((POOL * B0, ROW), np.uint8)
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    kf = torch.zeros((POOL * B0, ROWF), dtype=torch.uint8, device="cuda")
-    vf = torch.zeros((POOL * B0, ROWF), dtype=torch.uint8, device="cuda")
-    kf_ref = np.zeros((POOL * B0, ROWF), np.uint8)
-    vf_ref = np.zeros((POOL * B0, ROWF), np.uint8)
+    kf = [torch.zeros((POOL * B0, r), dtype=torch.uint8, device="cuda") for r in ROWF]
+    vf = [torch.zeros((POOL * B0, r), dtype=torch.uint8, device="cuda") for r in ROWF]
+    kf_ref = [np.zeros((POOL * B0, r), np.uint8) for r in ROWF]
+    vf_ref = [np.zeros((POOL * B0, r), np.uint8) for r in ROWF]
     counts = dict(corrections=0, bad_counts=0, kv_writes=0, sampled=0, truncations=0, fused=0)
 
     def row(rid):
@@ -161,13 +161,17 @@ def test_serving_loop_soak(rt):
         want = ref_step.compile_step(step_rows, block_size=B0, max_num_reqs=MR, max_model_len=M,
                                      max_num_batched_tokens=BUDGET, num_kv_blocks=POOL, n_pad=n_pad)
         fused = rng.random() < 0.25
-        if fused:                                                  # compile + K/V of 1 KiB rows in one kernel
-            srck = rng.integers(0, 256, (n_pad, ROWF), dtype=np.uint8)
-            srcv = rng.integers(0, 256, (n_pad, ROWF), dtype=np.uint8)
+        fi = step_no % 2                                           # which of the two row sizes
+        if fused:                                                  # compile + K/V in one kernel
+            rowf = ROWF[fi]
+            # always 1 KiB drawn (the seeded trajectory does not depend on fi);
+            # narrow steps use the first rowf bytes of each row
+            srck = np.ascontiguousarray(rng.integers(0, 256, (n_pad, ROWF[0]), dtype=np.uint8)[:, :rowf])
+            srcv = np.ascontiguousarray(rng.integers(0, 256, (n_pad, ROWF[0]), dtype=np.uint8)[:, :rowf])
             k_dev, v_dev = torch.from_numpy(srck).cuda(), torch.from_numpy(srcv).cuda()
             status.zero_()
-            s = ric.ric_compile_and_cache(b.h, n_pad, [k_dev.data_ptr()], [v_dev.data_ptr()], [kf.data_ptr()],
-                                          [vf.data_ptr()], ROWF, POOL * B0, dev_status=status.data_ptr(),
+            s = ric.ric_compile_and_cache(b.h, n_pad, [k_dev.data_ptr()], [v_dev.data_ptr()], [kf[fi].data_ptr()],
+                                          [vf[fi].data_ptr()], rowf, POOL * B0, dev_status=status.data_ptr(),
                                           flags=ric.RIC_FUSE_ALWAYS)
         else:
             s = b.compile(n_pad)
@@ -184,11 +188,11 @@ def test_serving_loop_soak(rt):
         if fused:
             assert int(status.item()) == 0, step_no
             slots = np.asarray(want["slot_mapping"][:N], np.int64)
-            kf_ref[slots] = srck[:N]
-            vf_ref[slots] = srcv[:N]
+            kf_ref[fi][slots] = srck[:N]
+            vf_ref[fi][slots] = srcv[:N]
             touched = torch.from_numpy(np.unique(slots)).cuda()
-            assert np.array_equal(kf[touched].cpu().numpy(), kf_ref[touched.cpu().numpy()]), step_no
-            assert np.array_equal(vf[touched].cpu().numpy(), vf_ref[touched.cpu().numpy()]), step_no
+            assert np.array_equal(kf[fi][touched].cpu().numpy(), kf_ref[fi][touched.cpu().numpy()]), step_no
+            assert np.array_equal(vf[fi][touched].cpu().numpy(), vf_ref[fi][touched.cpu().numpy()]), step_no
             counts["fused"] += 1
 
         if rng.random() < 0.2:                                     # this step's K/V rows
