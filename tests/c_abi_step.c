@@ -1,6 +1,7 @@
 /* One step through the C ABI from plain C (no C++, no Python): the worked
  * example of the first page ("vLLM 源码完全拆解（五）…", sections 1-5: three
- * requests, block size 4), compiled and its K/V rows written, outputs printed
+ * requests, block size 4), compiled and its K/V rows written (by the two
+ * separate calls, then again by ric_compile_and_cache), outputs printed
  * as one JSON object for the test that runs this program to compare with the
  * page's values.  Device memory for the K/V sources and caches comes from the
  * HIP runtime's C API; everything else goes through ric.h. */
@@ -12,6 +13,8 @@
 #include <hip/hip_runtime_api.h>
 
 #include "ric.h"
+
+#define ROW2 128   /* rows the single compile + K/V kernel takes */
 
 #define CHECK(x)                                                                     \
     do {                                                                             \
@@ -91,6 +94,32 @@ int main(void) {
     uint8_t cache_host[SLOTS * ROW];
     CHECK(ric_read_device(cache_host, k_cache, sizeof cache_host));
 
+    /* The same step again through ric_compile_and_cache, with 128-byte rows
+     * (compile and K/V write in one kernel), into caches of their own. */
+    void *k2_src, *v2_src, *k2_cache, *v2_cache;
+    if (hipMalloc(&k2_src, NPAD * ROW2) || hipMalloc(&v2_src, NPAD * ROW2) || hipMalloc(&k2_cache, SLOTS * ROW2) ||
+        hipMalloc(&v2_cache, SLOTS * ROW2)) {
+        fprintf(stderr, "hipMalloc failed\n");
+        return 1;
+    }
+    uint8_t host2[NPAD * ROW2];
+    for (int t = 0; t < NPAD; ++t) memset(host2 + t * ROW2, t + 1, ROW2);
+    if (hipMemcpy(k2_src, host2, sizeof host2, hipMemcpyHostToDevice) ||
+        hipMemcpy(v2_src, host2, sizeof host2, hipMemcpyHostToDevice) || hipMemset(k2_cache, 0, SLOTS * ROW2) ||
+        hipMemset(v2_cache, 0, SLOTS * ROW2)) {
+        fprintf(stderr, "hipMemcpy failed\n");
+        return 1;
+    }
+    const void* ks2[1] = {k2_src};
+    const void* vs2[1] = {v2_src};
+    void* kc2[1] = {k2_cache};
+    void* vc2[1] = {v2_cache};
+    CHECK(ric_schedule(b, R, c, q));
+    ric_step s2;
+    CHECK(ric_compile_and_cache(b, NPAD, ks2, vs2, kc2, vc2, 1, 0, ROW2, SLOTS, NULL, 0, &s2));
+    uint8_t cache2_host[SLOTS * ROW2];
+    CHECK(ric_read_device(cache2_host, v2_cache, sizeof cache2_host));
+
     printf("{\n\"num_reqs\": %d, \"num_actual_tokens\": %d, \"num_tokens_padded\": %d,\n", s.num_reqs,
            s.num_actual_tokens, s.num_tokens_padded);
     printf("\"max_query_len\": %d, \"max_seq_len\": %d, \"num_sampled\": %d,\n", s.max_query_len, s.max_seq_len,
@@ -106,12 +135,20 @@ int main(void) {
     print_array("sample_indices", s.sample_indices, R, 0);
     printf("\"k_cache_first_byte\": [");
     for (int i = 0; i < SLOTS; ++i) printf("%s%d", i ? ", " : "", cache_host[i * ROW]);
+    printf("],\n");
+    print_array("fused_slot_mapping", s2.slot_mapping, NPAD, 0);
+    printf("\"fused_v_cache_first_byte\": [");
+    for (int i = 0; i < SLOTS; ++i) printf("%s%d", i ? ", " : "", cache2_host[i * ROW2]);
     printf("]\n}\n");
 
     hipFree(k_src);
     hipFree(v_src);
     hipFree(k_cache);
     hipFree(v_cache);
+    hipFree(k2_src);
+    hipFree(v2_src);
+    hipFree(k2_cache);
+    hipFree(v2_cache);
     CHECK(ric_destroy(b));
     return 0;
 }

@@ -681,7 +681,8 @@ def test_strided_sources_from_a_fused_qkv_tensor(rt):
 def test_c_program_through_the_abi(rt, tmp_path):
     """A plain-C program (tests/c_abi_step.c) runs the first page's worked
     example through ric.h: its printed outputs equal the page's values, and
-    its K/V rows land at the printed slots."""
+    its K/V rows land at the printed slots, through the separate calls and
+    through ric_compile_and_cache."""
     import json
     import subprocess
     from tests.test_abi import build_c_step
@@ -700,10 +701,14 @@ def test_c_program_through_the_abi(rt, tmp_path):
     assert got["req_indices"][N:] == [-1, -1] and got["slot_mapping"][N:] == [0, 0]
     assert got["cu_seqlens_k"] == [0, 6, 9, 19]
     assert got["sample_indices"] == [0, 5, -1]          # B's chunk is discarded
-    first = got["k_cache_first_byte"]
-    for t, s in enumerate(g["slot_mapping"]):
-        assert first[s] == t + 1
-    assert all(first[i] == 0 for i in range(4, len(first)) if i not in g["slot_mapping"])
+    # both writes: the separate calls (64-byte rows) and ric_compile_and_cache
+    # (128-byte rows, one kernel), whose compile equals the first
+    assert got["fused_slot_mapping"] == got["slot_mapping"]
+    for name in ("k_cache_first_byte", "fused_v_cache_first_byte"):
+        first = got[name]
+        for t, s in enumerate(g["slot_mapping"]):
+            assert first[s] == t + 1, name
+        assert all(first[i] == 0 for i in range(4, len(first)) if i not in g["slot_mapping"]), name
 
 
 def test_debug_dump_prints_the_step(rt, capsys):
