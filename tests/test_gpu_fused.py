@@ -1,5 +1,5 @@
 """ric_compile_and_cache (the compile and the K/V write of up to 32 layers in
-one kernel for 1, 2 and 4 KiB rows) against the CPU oracle: every compile
+one kernel for rows of 128 B to 8 KiB) against the CPU oracle: every compile
 output bit-exact, every byte of every cache (real rows at the oracle's slots,
 the sentinel everywhere else outside the null block), on the full-size
 configurations, on random batches across block sizes, row sizes and padded
@@ -317,8 +317,9 @@ def test_fused_at_the_row_limit(rt):
 
 def test_fused_long_runs(rt):
     """Steps of long per-request runs (1024 or more scheduled tokens per
-    request on average), alternately through the single kernel's long-run
-    tile shape and the library's own choice (two kernels), 24 seeded
+    request on average), alternately forced onto the single kernel and
+    through the library's own choice (two kernels for rows of 1 KiB or more),
+    24 seeded
     batches: 1-8 requests, chunks of 1024-4096 tokens on cached prefixes up to
     4000, block sizes 1, 16, 64 and 100, rows of 256 B, 512 B, 1, 2 and 4
     KiB (the narrow ones take the single kernel by the library's own choice
