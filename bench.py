@@ -887,6 +887,12 @@ def extra_config(ric, runner, torch, workloads, name, steps, warmup, with_next_r
            "step_bytes": sb["total"], "library_path": path, "compile_plus_kv": ck,
            "dominant_kernel": kernel, "dominant_kernel_traffic": load_traffic(kernel, name),
            "rotation_instances": len(sets), "seconds": None}
+    # a plain copy of this step's K/V bytes on the same GPU, and how compile +
+    # K/V (the library's path, warm) compares with it
+    cc = copy_ceiling(ric, torch, sets, w0, sb)
+    fastest = min(cc["torch_copy_us"], cc["identity_slots_us"])
+    cc["compile_plus_kv_over_copy"] = ck["auto"]["warm_us"] / fastest
+    res["copy_ceiling"] = cc
     if sets[0].gather_rows:
         # the gather alone (events around it, rotating instances): M rows of
         # hidden states read and written, plus the M indices
