@@ -110,8 +110,24 @@ def fused_path(w):
     return w.row_bytes in (1024, 2048, 3072, 4096, 6144, 8192) and N < 1024 * max(len(live), 1)
 
 
-def dominant_kernel(w, n_pad):
-    return "compile_kv_kernel" if fused_path(w) else kv_kernel_name(w, n_pad)
+def dominant_kernel(w, n_pad, fused=None):
+    """The step's dominant kernel: the single compile + K/V kernel when the
+    library takes it (`fused`; default: the mirror of its rule), else the
+    separate K/V kernel."""
+    fused = fused_path(w) if fused is None else fused
+    return "compile_kv_kernel" if fused else kv_kernel_name(w, n_pad)
+
+
+def library_takes_single_kernel(st, w):
+    """Whether ric_compile_and_cache took the single kernel for this step by
+    its own choice, as the call reports it (ric_step.kv_path); the bench's
+    mirror of the rule must agree."""
+    st.compile_kv(0)
+    fused = int(st.step_out.kv_path) == 1
+    if fused != fused_path(w):
+        raise RuntimeError(f"{w.name}: the library took kv_path {int(st.step_out.kv_path)}, the bench's mirror "
+                           f"of its rule expected {'1' if fused_path(w) else '2'}")
+    return fused
 
 
 def code_digest(text):
@@ -880,8 +896,9 @@ def extra_config(ric, runner, torch, workloads, name, steps, warmup, with_next_r
     flush_buf = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
     ck = compile_kv_paths(torch, sets, sb, 30, 10, flush_buf)
     del flush_buf
-    path = "single_kernel" if fused_path(w0) else "two_kernels"
-    kernel = dominant_kernel(w0, sets[0].n_pad)
+    fused = library_takes_single_kernel(sets[0], w0)
+    path = "single_kernel" if fused else "two_kernels"
+    kernel = dominant_kernel(w0, sets[0].n_pad, fused)
     res = {"workload": f"{name}: {DESCRIPTIONS[name]}", "num_reqs": sb["R"], "num_tokens": sb["N"],
            "num_layers": w0.num_layers, "tokens_per_s": sb["N"] / (ms * 1e-3), "ms_per_step": ms,
            "step_bytes": sb["total"], "library_path": path, "compile_plus_kv": ck,
@@ -927,8 +944,8 @@ def main():
     w0, sb, sets = build_sets(ric, runner, torch, workloads, args.config, args.sets)
     S = len(sets)
     setup_s = time.perf_counter() - t_setup
-    fused = fused_path(w0)
-    kernel = dominant_kernel(w0, sets[0].n_pad)
+    fused = library_takes_single_kernel(sets[0], w0)
+    kernel = dominant_kernel(w0, sets[0].n_pad, fused)
 
     # The timed region: whole steps, no events.
     ms_per_step = timed_steps(torch, sets, args.steps, args.warmup)

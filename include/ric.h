@@ -128,6 +128,9 @@ typedef struct {
     int32_t max_query_len;
     int32_t max_seq_len;
     int32_t num_sampled;
+    int32_t kv_path;           /* which launches this call made: 0 the compile only (ric_compile),
+                                  1 the compile and the K/V write in one kernel, 2 the compile
+                                  kernel followed by the K/V kernel (ric_compile_and_cache) */
 } ric_step;
 
 /* Device views of the column store (for inspection and tests).  Row r of the

@@ -56,7 +56,7 @@ class ric_step(ctypes.Structure):
                 ("sample_indices", _vp), ("dev_scalars", _vp), ("cu_seqlens_k", _vp),
                 ("group_slot_mapping", _vp * RIC_MAX_KV_GROUPS)] + \
                [(n, ctypes.c_int32) for n in ("num_reqs", "num_actual_tokens", "num_tokens_padded",
-                                              "max_query_len", "max_seq_len", "num_sampled")]
+                                              "max_query_len", "max_seq_len", "num_sampled", "kv_path")]
 
 
 class ric_columns(ctypes.Structure):

@@ -1145,6 +1145,7 @@ void fill_step(const ric_batch* b, int32_t n_pad, ric_step* out) {
     out->max_query_len = b->sched_max_q;
     out->max_seq_len = b->sched_max_seq;
     out->num_sampled = b->sched_sampled;
+    out->kv_path = 0;
 }
 
 int check_compile_args(const ric_batch* b, int32_t n_pad) {
@@ -1266,6 +1267,7 @@ int ric_compile_and_cache(ric_batch* b, int32_t n_pad, const void* const* k, con
     }
     b->compiled = true;
     fill_step(b, n_pad, out);
+    if (out) out->kv_path = fuse ? 1 : 2;
     return RIC_OK;
 }
 

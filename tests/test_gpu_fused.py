@@ -34,6 +34,21 @@ def _prepare(rt, w):
     return b, exp
 
 
+def _expected_path(w, exp, flags):
+    """The path ric_compile_and_cache reports (ric_step.kv_path) by its rule:
+    1 (one kernel) for rows of 128, 256 or 512 B or 1, 2, 3, 4, 6 or 8 KiB,
+    unless flags force two kernels or the rows are 1 KiB or more and the step
+    averages 1024 or more tokens per request (without RIC_FUSE_ALWAYS); else
+    2 (the compile kernel, then the K/V kernel)."""
+    supported = w.row_bytes in (128, 256, 512, 1024, 2048, 3072, 4096, 6144, 8192)
+    long_runs = exp["num_actual_tokens"] >= 1024 * max(exp["num_reqs"], 1)
+    if not supported or flags == NEVER or exp["n_pad"] == 0:
+        return 2
+    if flags == ALWAYS:
+        return 1
+    return 2 if (long_runs and w.row_bytes >= 1024) else 1
+
+
 def _fused_step(rt, w, b, exp, sentinel, host_sources=False, layers=None, flags=0):
     ric, runner = rt
     L = w.num_layers if layers is None else layers
@@ -46,6 +61,7 @@ def _fused_step(rt, w, b, exp, sentinel, host_sources=False, layers=None, flags=
     assert int(status.item()) == 0
     assert (s.num_reqs, s.num_actual_tokens, s.num_tokens_padded) == (exp["num_reqs"], exp["num_actual_tokens"],
                                                                       exp["n_pad"])
+    assert s.kv_path == _expected_path(w, exp, flags), (w.name, w.row_bytes, flags, s.kv_path)
     return s, kv
 
 

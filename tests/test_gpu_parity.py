@@ -40,8 +40,8 @@ def _compile(rt, w):
     assert n_pad == exp["n_pad"]
     s = b.compile(n_pad)
     assert (s.num_reqs, s.num_actual_tokens, s.num_tokens_padded, s.max_query_len, s.max_seq_len,
-            s.num_sampled) == (exp["num_reqs"], exp["num_actual_tokens"], n_pad, exp["max_query_len"],
-                               exp["max_seq_len"], exp["num_sampled"])
+            s.num_sampled, s.kv_path) == (exp["num_reqs"], exp["num_actual_tokens"], n_pad, exp["max_query_len"],
+                                          exp["max_seq_len"], exp["num_sampled"], 0)
     return b, s, ref, order, exp, moved
 
 
