@@ -47,8 +47,10 @@ DESCRIPTIONS = {
     "long_context": "4 requests x 8192-token chunks of 131072-token prompts, cached prefix U[0,122880], "
                     "block 64, bf16 K/V 8x128, 1 layer, compacted hidden gather",
     "long_context_forced": "long_context with request 0 at its last chunk (one compacted gather row)",
+    "long_context_tp8": "long_context as one rank of 8-way tensor parallelism sees it: one K/V head of 128 "
+                        "(256-byte rows), same schedule",
 }
-EXTRA_CONFIGS = ["worked_example", "decode_heavy", "mixed", "churn", "long_context"]
+EXTRA_CONFIGS = ["worked_example", "decode_heavy", "mixed", "churn", "long_context", "long_context_tp8"]
 
 
 def parse():

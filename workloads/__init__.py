@@ -20,6 +20,7 @@ replacement from ``[1, num_kv_blocks)``; block 0 is the reserved null block.
 """
 from __future__ import annotations
 
+import dataclasses
 from dataclasses import dataclass, field
 from typing import List, Optional
 
@@ -238,9 +239,18 @@ def long_context(force_complete: bool = False, variant: int = 0) -> Workload:
                     gather="compacted", initial=reqs, seed=SEED_BASE + 4 + (variant << 8))
 
 
+def long_context_tp8(variant: int = 0) -> Workload:
+    """long_context as one rank of an 8-way tensor-parallel split sees it: the
+    same requests, schedule and block tables, one K/V head of 128 (256-byte
+    rows) instead of eight."""
+    w = long_context(False, variant)
+    return dataclasses.replace(w, name="long_context_tp8", kv_heads=1)
+
+
 _BUILDERS = {"worked_example": worked_example, "decode_heavy": decode_heavy,
              "mixed": mixed, "churn": churn, "long_context": long_context,
-             "long_context_forced": lambda variant=0: long_context(True, variant)}
+             "long_context_forced": lambda variant=0: long_context(True, variant),
+             "long_context_tp8": long_context_tp8}
 
 
 def get(name: str, variant: int = 0) -> Workload:
