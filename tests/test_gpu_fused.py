@@ -121,6 +121,26 @@ def test_fused_full_size_narrow_rows(rt, name, heads):
     b.close()
 
 
+VARIANTS = [(n, v) for n in ("churn", "mixed", "decode_heavy", "long_context") for v in (1, 2)]
+
+
+@pytest.mark.parametrize("name,variant", VARIANTS, ids=[f"{n}-{v}" for n, v in VARIANTS])
+def test_fused_other_seeded_instances(rt, name, variant):
+    """Independently seeded instances of the full-size configurations (the
+    ones the benchmark rotates over) through the library's own choice of
+    path: every compile output and every row of every K/V cache against the
+    oracle."""
+    w = workloads.get(name, variant=variant)
+    b, exp = _prepare(rt, w)
+    sentinel = 0x3A3A
+    s, kv = _fused_step(rt, w, b, exp, sentinel, flags=0)
+    assert_step_equal(b.step_outputs(s), exp, f"{name} instance {variant}")
+    _check_all(w, exp, kv, sentinel, f"{name} instance {variant}")
+    del kv
+    torch.cuda.empty_cache()
+    b.close()
+
+
 def _random_workload(rng, trial, head_choices):
     B = int(rng.choice([1, 2, 3, 4, 8, 16, 32, 64]))
     R = int(rng.integers(1, 300))
