@@ -385,3 +385,46 @@ def test_fused_long_runs(rt):
         assert_step_equal(b.step_outputs(s), exp, label)
         _check_all(w, exp, kv, 0x5A5A, label)
         b.close()
+
+
+def test_two_handles_on_two_streams(rt):
+    """Two handles, each on its own stream, their calls interleaved with no
+    synchronisation between them (mixed through the single kernel, the
+    worked example through the single kernel with 256 B rows, then each
+    scheduled and compiled again): per-handle state is separate, so both
+    steps equal the oracle's."""
+    ric, runner = rt
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    made = []
+    for name, st in (("mixed", s1), ("worked_example", s2)):
+        w = workloads.get(name)
+        with torch.cuda.stream(st):
+            b = runner.Batch(runner.config_of(w), stream=runner.current_stream())
+            for r in w.initial:
+                b.add(r)
+            for rid in w.finished:
+                ric.ric_remove_request(b.h, rid)
+            if w.finished:
+                ric.ric_condense(b.h)
+            for r in w.refill:
+                b.add(r)
+        ref, order = replay_history(w)
+        exp = expected_step(w, ref, use_python=(name == "worked_example"))
+        kc, vc = runner.alloc_caches(w, fill=0x1111)
+        k, v = runner.alloc_sources(w, exp["n_pad"], seed=w.seed + 77)
+        made.append((name, w, st, b, order, exp, runner.KVSet(k, v, kc, vc, w.row_bytes,
+                                                               w.num_kv_blocks * w.block_size)))
+    torch.cuda.synchronize()
+    for rep in range(3):
+        steps = []
+        for name, w, st, b, order, exp, kv in made:     # enqueue both, then wait once
+            with torch.cuda.stream(st):
+                b.schedule_from(w, order)
+                steps.append(runner.compile_and_cache(b, exp["n_pad"], kv))
+        torch.cuda.synchronize()
+        for (name, w, st, b, order, exp, kv), s in zip(made, steps):
+            assert s.kv_path == 1, (name, s.kv_path)
+            assert_step_equal(b.step_outputs(s), exp, f"{name} round {rep}")
+            _check_all(w, exp, kv, 0x1111, f"{name} round {rep}")
+    for m in made:
+        m[3].close()
